@@ -1,0 +1,37 @@
+"""fp64 CPU oracle for exact (FlashAttention-style) attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, helpers, headers, constants or pre/post-processing) and
+imports nothing from the package ``exact_tiled_attention_fa_amd``.
+
+Contents
+--------
+``attention.attention_ref``
+    The plain definition of softmax attention (scores, mask, row softmax,
+    weighted sum of values, per-row logsumexp), evaluated in float64.
+``attention.decode_ref``
+    The same definition for one query token per sequence against a padded
+    KV cache with per-sequence lengths.
+``online.online_attention_ref`` / ``online.split_combine_ref``
+    The blockwise online-softmax recurrence and the logsumexp merge of
+    key-chunk summaries, restated in float64 from the pages.  These are
+    checked against ``attention_ref`` (the pages claim the two agree exactly)
+    and are never used as the reference for the GPU.
+
+Every function is pinned by tests in ``tests/test_oracle.py`` to things other
+than itself: a 40-digit ``decimal`` brute force, PyTorch's fp64 CPU
+``scaled_dot_product_attention``, closed forms and invariants.
+"""
+
+from .attention import attention_ref, decode_ref, causal_allowed
+from .online import online_attention_ref, split_combine_ref
+
+__all__ = [
+    "attention_ref",
+    "decode_ref",
+    "causal_allowed",
+    "online_attention_ref",
+    "split_combine_ref",
+]

@@ -1,0 +1,194 @@
+"""Plain softmax attention in float64 -- the oracle's definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+What is computed, and where the pages fix it
+--------------------------------------------
+For batch b, query head h, key/value head kv = floor(h / (Hq / Hkv)) and query
+row i:
+
+  s_ij   = scale * sum_d q[b,i,h,d] * k[b,j,kv,d]              (scaled scores)
+  A_i    = { j : not causal  or  j <= i + (Lk - Lq) }          (allowed keys)
+  m_i    = max_{j in A_i} s_ij
+  l_i    = sum_{j in A_i} exp(s_ij - m_i)
+  P_ij   = exp(s_ij - m_i) / l_i  on A_i,  0 elsewhere
+  O[b,i,h,:] = sum_j P_ij * v[b,j,kv,:]
+  lse[b,h,i] = m_i + ln l_i                                   (natural log)
+  A_i empty  ->  O = 0, lse = -inf
+
+Sources (page title, section):
+* "FlashAttention in the CANN ops-transformer library" (ai6s.net), section 1:
+  the standard computation materialises Q K^T and its softmax (O(N^2)); the
+  method tiles it and must give the same result (section 2, step 2).
+* same page, section 2 step 3: an output O and a per-row normaliser L are
+  produced.  Read here as L = the per-row logsumexp of the scaled scores over
+  the allowed keys, natural log, laid out [B, Hq, Lq].
+* same page, section 4 (usage): arguments q, k, v in [batch, seq, heads,
+  head_dim] layout, ``softmax_scale`` defaulting to 1/sqrt(head_dim),
+  ``is_causal``; section 5: causal keys "above the diagonal" take no part in
+  the softmax (their probability is 0; the page's "scores set to zero" is read
+  as probabilities zero, since it also says they leave the softmax), and
+  bidirectional (BERT-style) use has no mask.
+* "Enable Flash Attention with llama.cpp" (qualllm.com), FAQ on GQA, and
+  "MNN LLM attention_mode" (lpnh.cn), section on choosing a mode: K/V heads
+  shared by groups of query heads (group 1/2/4/8).  Read as consecutive query
+  heads sharing one K/V head.
+* Causal alignment when Lq != Lk is not on the pages; read as bottom-right
+  (the last query row sees every key), which equals the usual lower triangle
+  when Lq == Lk and makes a one-token decode see its whole cache.
+
+Implementation notes: each (b, h) pair is independent; rows are processed in
+blocks of ``row_block`` so that at most row_block x Lk scores exist at once.
+That is still the plain definition -- each row's max, sum and weighted sum run
+over its whole allowed key set.  Under causal masking, keys that no row of the
+block may see are simply not formed (their probability is exactly 0).
+"""
+
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+try:  # keep BLAS single-threaded inside the (b, h) worker pool
+    from threadpoolctl import threadpool_limits
+except Exception:  # pragma: no cover - optional
+    threadpool_limits = None
+
+
+def causal_allowed(i: int, Lq: int, Lk: int) -> int:
+    """Largest key index query row ``i`` may attend to under the causal mask
+    (bottom-right alignment: j <= i + Lk - Lq).  Negative means none."""
+    return i + (Lk - Lq)
+
+
+def _as_f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor -> exact float64 copy
+        import torch
+
+        x = x.detach().to("cpu").to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _head_attention(qh, kh, vh, scale, causal, row_block):
+    """Plain attention for one (batch, head): qh [Lq,D], kh/vh [Lk,D]."""
+    Lq, D = qh.shape
+    Lk = kh.shape[0]
+    Dv = vh.shape[1]
+    out = np.zeros((Lq, Dv), dtype=np.float64)
+    lse = np.full((Lq,), -np.inf, dtype=np.float64)
+    if Lk == 0:
+        return out, lse
+    shift = Lk - Lq
+    for r0 in range(0, Lq, row_block):
+        r1 = min(Lq, r0 + row_block)
+        kend = Lk
+        if causal:
+            kend = min(Lk, (r1 - 1) + shift + 1)
+            if kend <= 0:
+                continue  # every row of this block has an empty key set
+        s = scale * (qh[r0:r1] @ kh[:kend].T)  # [rows, kend]
+        if causal:
+            rows = np.arange(r0, r1)[:, None]
+            cols = np.arange(kend)[None, :]
+            s = np.where(cols <= rows + shift, s, -np.inf)
+        m = s.max(axis=1)
+        nonempty = np.isfinite(m)
+        m_safe = np.where(nonempty, m, 0.0)
+        p = np.exp(s - m_safe[:, None])  # exp(-inf) = 0 on masked keys
+        l = p.sum(axis=1)
+        o = p @ vh[:kend]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            o = np.where(nonempty[:, None], o / l[:, None], 0.0)
+            blk_lse = np.where(nonempty, m_safe + np.log(l), -np.inf)
+        out[r0:r1] = o
+        lse[r0:r1] = blk_lse
+    return out, lse
+
+
+def _default_workers() -> int:
+    env = os.environ.get("ORACLE_WORKERS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def attention_ref(q, k, v, scale: float, causal: bool, *, row_block: int = 1024,
+                  workers: int | None = None, heads=None):
+    """Plain fp64 attention.
+
+    q: [B, Lq, Hq, D]; k, v: [B, Lk, Hkv, D] (any float type; converted to
+    float64 exactly).  ``scale`` is applied as given (pass the float32 value
+    that the GPU receives).  Returns (O [B, Lq, Hq, D], lse [B, Hq, Lq]) in
+    float64.  ``heads`` optionally restricts the work to a list of (b, h)
+    pairs; other outputs are left as NaN.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    B, Lq, Hq, D = q.shape
+    Bk, Lk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D or v.shape[:3] != k.shape[:3]:
+        raise ValueError("shape mismatch between q, k, v")
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    scale = float(scale)
+    out = np.full((B, Lq, Hq, v.shape[3]), np.nan)
+    lse = np.full((B, Hq, Lq), np.nan)
+    jobs = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+
+    def run(job):
+        b, h = job
+        kv = h // g
+        o, l = _head_attention(q[b, :, h, :], k[b, :, kv, :], v[b, :, kv, :],
+                               scale, causal, row_block)
+        out[b, :, h, :] = o
+        lse[b, h, :] = l
+
+    nw = workers if workers is not None else _default_workers()
+    if nw <= 1 or len(jobs) <= 1:
+        for j in jobs:
+            run(j)
+    else:
+        import contextlib
+        ctx = threadpool_limits(limits=1) if threadpool_limits is not None else contextlib.nullcontext()
+        with ctx, ThreadPoolExecutor(max_workers=nw) as ex:
+            list(ex.map(run, jobs))
+    return out, lse
+
+
+def decode_ref(q, k_cache, v_cache, seqlens, scale: float, *, heads=None):
+    """One query token per sequence against a padded KV cache.
+
+    q: [B, Hq, D]; k_cache, v_cache: [B, Lk_max, Hkv, D]; seqlens: [B] ints.
+    Sequence b attends to keys 0 .. seqlens[b]-1 (all of them: the query is
+    the newest token, so the bottom-right causal mask admits its whole
+    cache).  Padding rows beyond seqlens[b] are never read.  Returns
+    (O [B, Hq, D], lse [B, Hq]) in float64.
+    """
+    q = _as_f64(q)
+    B, Hq, D = q.shape
+    lens = [int(x) for x in np.asarray(seqlens).reshape(-1)]
+    Hkv = k_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    out = np.full((B, Hq, v_cache.shape[3]), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    jobs = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    cache_k, cache_v = {}, {}
+    for b, h in jobs:
+        kv = h // g
+        n = max(0, min(lens[b], k_cache.shape[1]))
+        key = (b, kv)
+        if key not in cache_k:  # slice first: padding (possibly NaN) is never touched
+            cache_k[key] = _as_f64(k_cache[b, :n, kv, :])
+            cache_v[key] = _as_f64(v_cache[b, :n, kv, :])
+        o, l = _head_attention(q[b, h, :][None, :], cache_k[key], cache_v[key],
+                               float(scale), False, 1)
+        out[b, h, :] = o[0]
+        lse[b, h] = l[0]
+    return out, lse

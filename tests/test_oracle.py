@@ -1,0 +1,137 @@
+"""The oracle, pinned to things other than itself (CPU only)."""
+
+from __future__ import annotations
+
+import inspect
+import textwrap
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oatt
+from pins import ALL_PINS, assert_close, rand_qkv
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle.attention_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [1, 7, 64, None])
+def test_online_equals_two_pass(causal, block):
+    """The pages' blockwise online softmax reaches the standard result."""
+    q, k, v = rand_qkv(11, 2, 37, 37, 4, 2, 16, scale_q=2.0)
+    o1, l1 = oracle.attention_ref(q, k, v, 0.3, causal)
+    o2, l2 = oracle.online_attention_ref(q, k, v, 0.3, causal, block or 37)
+    assert_close(o2, o1, 1e-12, "online O")
+    assert_close(l2, l1, 1e-12, "online lse")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [1, 2, 8, 13])
+def test_split_combine_equals_two_pass(causal, splits):
+    q, k, v = rand_qkv(12, 1, 23, 29, 2, 1, 8, scale_q=2.0)
+    o1, l1 = oracle.attention_ref(q, k, v, 0.4, causal)
+    o2, l2 = oracle.split_combine_ref(q, k, v, 0.4, causal, splits)
+    assert_close(o2, o1, 1e-12, "split O")
+    assert_close(l2, l1, 1e-12, "split lse")
+
+
+def test_decode_equals_last_row_of_causal_prefill():
+    r = np.random.default_rng(13)
+    B, Hq, Hkv, D, Lmax = 3, 4, 2, 8, 20
+    lens = [20, 7, 1]
+    kc = r.standard_normal((B, Lmax, Hkv, D))
+    vc = r.standard_normal((B, Lmax, Hkv, D))
+    q = r.standard_normal((B, Hq, D))
+    o, l = oracle.decode_ref(q, kc, vc, lens, 0.35)
+    for b in range(B):
+        n = lens[b]
+        qq = np.zeros((1, n, Hq, D))
+        qq[0, n - 1] = q[b]
+        op, lp = oracle.attention_ref(qq, kc[b:b + 1, :n], vc[b:b + 1, :n], 0.35, True)
+        assert_close(o[b], op[0, n - 1], 1e-13, "decode O")
+        assert_close(l[b], lp[0, :, n - 1], 1e-13, "decode lse")
+
+
+def test_decode_never_reads_padding_and_handles_empty():
+    r = np.random.default_rng(14)
+    kc = np.full((2, 6, 1, 4), np.nan)
+    vc = np.full((2, 6, 1, 4), np.nan)
+    kc[0, :3] = r.standard_normal((3, 1, 4))
+    vc[0, :3] = r.standard_normal((3, 1, 4))
+    q = r.standard_normal((2, 2, 4))
+    o, l = oracle.decode_ref(q, kc, vc, [3, 0], 0.5)
+    assert np.all(np.isfinite(o[0])) and np.all(np.isfinite(l[0]))
+    assert np.all(o[1] == 0) and np.all(l[1] == -np.inf)
+
+
+def test_row_blocking_is_invisible():
+    q, k, v = rand_qkv(15, 1, 50, 50, 2, 2, 8)
+    for causal in (False, True):
+        o1, l1 = oracle.attention_ref(q, k, v, 0.3, causal, row_block=1024)
+        o2, l2 = oracle.attention_ref(q, k, v, 0.3, causal, row_block=7, workers=3)
+        assert_close(o2, o1, 1e-15, "row blocks O")
+        assert_close(l2, l1, 1e-15, "row blocks lse")
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each mutant is the oracle with one plausible bug written
+# into its source; at least one pin must reject it.
+# ---------------------------------------------------------------------------
+HEAD_MUTATIONS = {
+    "mask_off_by_one": ("cols <= rows + shift", "cols < rows + shift"),
+    "mask_top_left": ("cols <= rows + shift", "cols <= rows"),
+    "dropped_scale": ("s = scale * (qh[r0:r1] @ kh[:kend].T)", "s = (qh[r0:r1] @ kh[:kend].T)"),
+    "sign_flip": ("s = scale * (qh[r0:r1] @ kh[:kend].T)", "s = -scale * (qh[r0:r1] @ kh[:kend].T)"),
+    "value_rows_reversed": ("o = p @ vh[:kend]", "o = p @ vh[:kend][::-1]"),
+    "lse_drops_max": ("m_safe + np.log(l)", "np.log(l)"),
+    "no_max_subtraction": ("p = np.exp(s - m_safe[:, None])", "p = np.exp(s)"),
+    "no_normalisation": ("o / l[:, None]", "o"),
+    "drops_last_key": ("kend = min(Lk, (r1 - 1) + shift + 1)", "kend = min(Lk, (r1 - 1) + shift)"),
+    "transposed_operand": ("s = scale * (qh[r0:r1] @ kh[:kend].T)",
+                           "s = scale * (qh[r0:r1] @ kh[:kend].T).T[:r1 - r0, :kend] "
+                           "if kend == r1 - r0 else scale * (qh[r0:r1] @ kh[:kend].T)"),
+}
+REF_MUTATIONS = {
+    "gqa_modulo_mapping": ("kv = h // g", "kv = h % Hkv"),
+}
+
+
+def _mutant(fn, old, new):
+    src = textwrap.dedent(inspect.getsource(fn))
+    assert old in src, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new)
+    ns = dict(vars(oatt))
+    exec(compile(src, f"<mutant {fn.__name__}>", "exec"), ns)
+    return ns[fn.__name__], ns
+
+
+def _rejected(attn) -> list:
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(attn)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except (ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__ + "(error)")
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(HEAD_MUTATIONS))
+def test_planted_mistake_in_head_is_caught(name, monkeypatch):
+    old, new = HEAD_MUTATIONS[name]
+    mutated, _ = _mutant(oatt._head_attention, old, new)
+    monkeypatch.setattr(oatt, "_head_attention", mutated)
+    assert _rejected(oracle.attention_ref), f"no pin rejects mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(REF_MUTATIONS))
+def test_planted_mistake_in_head_mapping_is_caught(name):
+    old, new = REF_MUTATIONS[name]
+    mutated, _ = _mutant(oatt.attention_ref, old, new)
+    assert _rejected(mutated), f"no pin rejects mutant {name}"
