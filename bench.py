@@ -1,0 +1,259 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass over both halves of the path, with inputs resident in
+HBM before timing starts:
+  * prefill: fa_fwd on the Llama-2-7B-shaped causal workload
+    (B=4, Hq=Hkv=32, L=4096, D=128, bf16);
+  * decode: fa_decode (split kernel + logsumexp combine) on 128 sequences,
+    Hq=32, Hkv=8, D=128, bf16, cache lengths uniform on [512, 8192], 8 splits.
+
+``value`` is the prefill throughput in algorithmic TFLOP/s (4*D per allowed
+query-key pair per query head) from HIP events around every prefill launch
+on the stream the kernel runs on; the decode half is reported in the same
+line as algorithmic HBM GB/s (K/V rows of each cache read once, q read, o and
+lse written).  ``ms_per_step`` is wall time per step over the K timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--with-copy MIB] [--only prefill|decode] [--all-configs]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (causal prefill) + decode HBM GB/s, % roofline"
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_fa_amd", "csrc")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the CPU oracle sample")
+    p.add_argument("--with-copy", type=int, default=0, metavar="MIB",
+                   help="after timing, run a plain device copy of MIB MiB (counter calibration)")
+    p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--all-configs", action="store_true",
+                   help="also print one extra JSON line per prefill workload")
+    return p.parse_args()
+
+
+def source_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, digest: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        e = t.get(kernel)
+        if e and e.get("source_digest") == digest:
+            return e.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline_prefill(cfg, q, k, v, scale, target_s):
+    """Time the fp64 oracle on a bounded sample of whole (batch, head) slices."""
+    import oracle
+    from oracle.attention import _default_workers
+
+    workers = _default_workers()
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    per_head_flops = cfg.flops() // len(pairs)
+    t0 = time.perf_counter()
+    oracle.attention_ref(q, k, v, scale, cfg.causal, heads=pairs[:1], workers=1)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(len(pairs), round(target_s / max(t1, 1e-3) * workers))))
+    n = max(workers, n - n % workers) if n >= workers else n
+    n = min(n, len(pairs))
+    t0 = time.perf_counter()
+    oracle.attention_ref(q, k, v, scale, cfg.causal, heads=pairs[:n], workers=workers)
+    dt = time.perf_counter() - t0
+    return {"value": round(per_head_flops * n / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": workers, "kind": "oracle",
+            "sample": f"{n} of {len(pairs)} (batch, head) slices of the same workload, "
+                      f"fp64 numpy, {dt:.2f} s wall"}
+
+
+def cpu_baseline_decode(cfg, q, kc, vc, lens, scale, nseq=16):
+    import oracle
+    from exact_tiled_attention_fa_amd import workloads as W
+
+    heads = [(b, h) for b in range(nseq) for h in range(cfg.Hq)]
+    t0 = time.perf_counter()
+    oracle.decode_ref(q, kc, vc, lens, scale, heads=heads)
+    dt = time.perf_counter() - t0
+    sub = lens[:nseq]
+    byts = int(sum(int(x) for x in sub)) * cfg.Hkv * cfg.D * 2 * 2 + nseq * cfg.Hq * (2 * cfg.D * 2 + 4)
+    return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {nseq} of {cfg.B} sequences, all heads, fp64 numpy, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
+                 "(run with --gpus 1).")
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import _abi
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import (decode_workspace, flash_attn_decode,
+                                                        flash_attn_fwd)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    info = _abi.fa_info()
+    do_pf = args.only in (None, "prefill")
+    do_dec = args.only in (None, "decode")
+
+    pcfg = W.PREFILL["llama7b"]
+    dcfg = W.DECODE["decode"]
+    pscale = float(np.float32(pcfg.scale))
+    dscale = float(np.float32(dcfg.scale))
+    print(f"# generating inputs ({pcfg.name}, {dcfg.name})", file=sys.stderr, flush=True)
+    if do_pf:
+        q_c, k_c, v_c = W.prefill_inputs(pcfg)
+        q, k, v = q_c.to(dev), k_c.to(dev), v_c.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((pcfg.B, pcfg.Hq, pcfg.L), dtype=torch.float32, device=dev)
+    if do_dec:
+        dq_c, kc_c, vc_c, lens_c = W.decode_inputs(dcfg)
+        dq, kc, vc, lens = dq_c.to(dev), kc_c.to(dev), vc_c.to(dev), lens_c.to(dev)
+        do_ = torch.empty_like(dq)
+        dlse = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device=dev)
+        ws = decode_workspace(dcfg.B, dcfg.Hq, dcfg.D, dcfg.num_splits, dev)
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        if do_pf:
+            flash_attn_fwd(q, k, v, softmax_scale=pscale, causal=True, out=o, lse=lse)
+        if evs is not None:
+            evs[1].record()
+        if do_dec:
+            flash_attn_decode(dq, kc, vc, lens, softmax_scale=dscale, num_splits=dcfg.num_splits,
+                              workspace=ws, out=do_, lse=dlse)
+        if evs is not None:
+            evs[2].record()
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pf_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+
+    if args.with_copy:
+        n = args.with_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    out = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) Q/K/V; no model weights)",
+           "config": {"workload": "llama7b causal prefill B=4 Hq=Hkv=32 L=4096 D=128 bf16 + "
+                                  "split-KV decode B=128 Hq=32 Hkv=8 D=128 bf16 len~U[512,8192] "
+                                  "8 splits",
+                      "prefill": {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "L": pcfg.L,
+                                  "D": pcfg.D, "causal": True},
+                      "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "D": dcfg.D,
+                                 "num_splits": dcfg.num_splits},
+                      "lib": info}}
+    if do_pf:
+        ms = float(np.mean(pf_ms))
+        tf = pcfg.flops() / (ms * 1e-3) / 1e12
+        out["value"] = round(tf, 3)
+        out["prefill_ms"] = {"mean": round(ms, 5), "median": round(float(np.median(pf_ms)), 5),
+                             "min": round(float(np.min(pf_ms)), 5)}
+        out["roofline"] = {"bound": "mfma", "achieved": round(tf, 3),
+                           "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                           "traffic": traffic_for("fwd_kernel", source_digest(
+                               ["fa_fwd.hip", "fa_common.hpp"])),
+                           "kernel": "fwd_kernel<bf16_t,128,64,true>",
+                           "alg_flops_per_launch": pcfg.flops()}
+    if do_dec:
+        dms = float(np.mean(dec_ms))
+        byts = W.decode_bytes(dcfg, lens_c)
+        gbs = byts / (dms * 1e-3) / 1e9
+        out["decode"] = {"value": round(gbs, 2), "unit": "GB/s",
+                         "ms": {"mean": round(dms, 5), "median": round(float(np.median(dec_ms)), 5),
+                                "min": round(float(np.min(dec_ms)), 5)},
+                         "alg_bytes_per_step": byts,
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 2),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                      "traffic": traffic_for("decode", source_digest(
+                                          ["fa_decode.hip", "fa_common.hpp"]))}}
+        if out["value"] is None:
+            out["value"], out["unit"] = round(gbs, 2), "GB/s"
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        if do_pf:
+            out["cpu_baseline"] = cpu_baseline_prefill(pcfg, q_c, k_c, v_c, pscale, args.cpu_seconds)
+        if do_dec:
+            out.setdefault("decode", {})["cpu_baseline"] = cpu_baseline_decode(
+                dcfg, dq_c, kc_c, vc_c, lens_c, dscale)
+    print(json.dumps(out), flush=True)
+
+    if args.all_configs:
+        for name, cfg in W.PREFILL.items():
+            qq, kk, vv = (t.to(dev) for t in W.prefill_inputs(cfg))
+            sc = float(np.float32(cfg.scale))
+            for _ in range(3):
+                flash_attn_fwd(qq, kk, vv, softmax_scale=sc, causal=cfg.causal)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            e0.record()
+            for _ in range(reps):
+                flash_attn_fwd(qq, kk, vv, softmax_scale=sc, causal=cfg.causal)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = cfg.flops() / (ms * 1e-3) / 1e12
+            print(json.dumps({"workload": name, "ms": round(ms, 5), "TFLOP/s": round(tf, 2),
+                              "frac_mfma": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                              "GB/s": round(cfg.hbm_bytes() / (ms * 1e-3) / 1e9, 1)}), flush=True)
+            del qq, kk, vv
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,91 @@
+"""ctypes binding of libfa's C ABI (include/fa.h), same names, marshalling only.
+
+The library is loaded on first use from ``_lib/libfa.so`` next to this file
+(override with the environment variable ``FA_GFX950_LIB``).  If it is missing
+every call raises -- there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+
+FA_F16 = 0
+FA_BF16 = 1
+
+STATUS_NAMES = {
+    FA_OK: "FA_OK",
+    FA_ERR_INVALID_ARGUMENT: "FA_ERR_INVALID_ARGUMENT",
+    FA_ERR_UNSUPPORTED: "FA_ERR_UNSUPPORTED",
+    FA_ERR_HIP: "FA_ERR_HIP",
+}
+
+# Every symbol include/fa.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
+    "fa_last_error": (ctypes.c_char_p, []),
+    "fa_info": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib_path() -> Path:
+    env = os.environ.get("FA_GFX950_LIB")
+    if env:
+        return Path(env)
+    return Path(__file__).resolve().parent / "_lib" / "libfa.so"
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once and attach the C signatures; raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not path.exists():
+        raise RuntimeError(
+            f"libfa.so not found at {path}; build it first with "
+            "`python -m exact_tiled_attention_fa_amd.build` (there is no fallback path)")
+    lib = ctypes.CDLL(str(path))
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype, stream) -> int:
+    """Raw C call; pointers are ints (device addresses), returns the status."""
+    return load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype, stream)
+
+
+def fa_decode_workspace_size(B, Hq, D, num_splits) -> int:
+    return load().fa_decode_workspace_size(B, Hq, D, num_splits)
+
+
+def fa_decode(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale, num_splits,
+              workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_decode(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale,
+                            num_splits, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_last_error() -> str:
+    return (load().fa_last_error() or b"").decode()
+
+
+def fa_info() -> str:
+    return (load().fa_info() or b"").decode()

@@ -1,0 +1,114 @@
+"""PyTorch-facing wrappers over libfa.  Torch supplies device memory and the
+current stream; every step of the computation runs in libfa's HIP kernels.
+
+The argument set follows the usage example of "FlashAttention in the CANN
+ops-transformer library" (ai6s.net), section 4: q, k, v in [batch, seq,
+heads, head_dim], ``dropout_p`` (only 0.0 is supported: this is the
+inference forward), ``softmax_scale`` (default 1/sqrt(head_dim)) and
+``is_causal``.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _abi
+
+_DTYPES = {torch.float16: _abi.FA_F16, torch.bfloat16: _abi.FA_BF16}
+
+
+class FAError(RuntimeError):
+    """A non-OK status from libfa; ``status`` holds the code."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_abi.STATUS_NAMES.get(status, status)}: {_abi.fa_last_error()}")
+
+
+def _check_dev(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, softmax_scale=None,
+                   causal: bool = False, dropout_p: float = 0.0, out=None, lse=None):
+    """Exact attention forward.  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] (fp16/bf16).
+
+    Returns (o [B,Lq,Hq,D] in q's dtype, lse [B,Hq,Lq] float32).  Causal
+    masking is bottom-right aligned (row i sees keys j <= i + Lk - Lq).
+    """
+    if dropout_p != 0.0:
+        raise ValueError("dropout_p must be 0.0 (the forward has no dropout)")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Lq,Hq,D] and k, v [B,Lk,Hkv,D] with equal shapes")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    B, Lq, Hq, D = q.shape
+    Bk, Lk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("batch or head_dim mismatch between q and k")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    st = _abi.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, Hq, Hkv, Lq, Lk, D, scale, 1 if causal else 0, _DTYPES[q.dtype],
+                     _stream_handle(q.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def decode_workspace(B: int, Hq: int, D: int, num_splits: int, device) -> torch.Tensor:
+    """A byte tensor large enough for fa_decode's workspace."""
+    n = _abi.fa_decode_workspace_size(B, Hq, D, num_splits)
+    if n == 0:
+        raise ValueError("invalid sizes for the decode workspace")
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def flash_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      seqlens: torch.Tensor, *, softmax_scale=None, num_splits: int = 8,
+                      workspace=None, out=None, lse=None):
+    """One query token per sequence.  q [B,Hq,D]; caches [B,Lk_max,Hkv,D];
+    seqlens int32 [B] on the device.  Returns (o [B,Hq,D], lse [B,Hq] float32).
+    """
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens, "seqlens")):
+        _check_dev(t, n)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,Hq,D] and k_cache, v_cache [B,Lk_max,Hkv,D]")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share dtype float16 or bfloat16")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (q.shape[0],):
+        raise ValueError("seqlens must be int32 [B]")
+    B, Hq, D = q.shape
+    _, Lk_max, Hkv, Dk = k_cache.shape
+    if k_cache.shape[0] != B or Dk != D:
+        raise ValueError("batch or head_dim mismatch between q and the caches")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, D, num_splits, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = _abi.fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                        out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Lk_max, D, scale, num_splits,
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                        _DTYPES[q.dtype], _stream_handle(q.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_decode")
+    return out, lse

@@ -1,0 +1,138 @@
+// C ABI of libfa (declared in include/fa.h): host-side validation, error
+// text and dispatch to the kernel launchers.  Nothing here touches the device
+// except the launches themselves; validation failures return before any HIP
+// call.
+#include "fa.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fa_status ok() {
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool head_dim_supported(int D) { return D == 64 || D == 128 || D == 256; }
+
+fa_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(FA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return FA_OK;
+}
+
+#define FA_TRY(expr)                  \
+  do {                                \
+    fa_status _st = (expr);           \
+    if (_st != FA_OK) return _st;     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int Lq, int Lk, int D, float scale, int causal, fa_dtype dtype,
+                 hipStream_t stream) {
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k, "k"));
+  FA_TRY(check_ptr(v, "v"));
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(lse, "lse"));
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || D < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d)", B, Hq, Hkv, Lq, Lk, D);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)dtype);
+  if (!head_dim_supported(D))
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", D);
+  const long long nqt = ((long long)Lq + fa::kFwdBM - 1) / fa::kFwdBM;
+  if (nqt * B * Hq > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (Lq/%d * B * Hq > 2^31-1)", fa::kFwdBM);
+  if ((long long)B * Lq * Hq > 0x7fffffffLL || (long long)B * Lk * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
+
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal ? 1 : 0,
+                dtype == FA_BF16 ? 1 : 0};
+  hipError_t e = fa::launch_fwd(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int D, int num_splits) {
+  if (B < 1 || Hq < 1 || D < 1 || num_splits < 1 || num_splits > 64) return 0;
+  return fa::decode_workspace_bytes(B, Hq, D, num_splits);
+}
+
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                    void* o, float* lse, int B, int Hq, int Hkv, int Lk_max, int D, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                    hipStream_t stream) {
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k_cache, "k_cache"));
+  FA_TRY(check_ptr(v_cache, "v_cache"));
+  if (!seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "seqlens is NULL");
+  if (((uintptr_t)seqlens & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "seqlens is not 4-byte aligned");
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(lse, "lse"));
+  FA_TRY(check_ptr(workspace, "workspace"));
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lk_max < 1 || D < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lk_max=%d D=%d)",
+                B, Hq, Hkv, Lk_max, D);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (num_splits < 1 || num_splits > 64)
+    return fail(FA_ERR_INVALID_ARGUMENT, "num_splits=%d not in [1, 64]", num_splits);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)dtype);
+  if (!head_dim_supported(D))
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", D);
+  if ((long long)B * Lk_max * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*Lk_max*Hkv exceeds 2^31-1 rows");
+  if ((long long)Hkv * ((Hq / Hkv + 15) / 16) > 65535 || B > 65535)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (B or Hq exceeds 65535)");
+  const size_t need = fa::decode_workspace_bytes(B, Hq, D, num_splits);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                need);
+
+  fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale,
+                   num_splits, workspace, dtype == FA_BF16 ? 1 : 0};
+  hipError_t e = fa::launch_decode(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+const char* fa_info(void) {
+  return "arch=gfx950; head_dims={64,128,256}; dtypes={f16,bf16}; "
+         "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), BN=64 keys, "
+         "mfma_f32_32x32x16, K/V^T tiles in LDS, causal tile skip, GQA; "
+         "decode: split-KV, 1 wave64 per (chunk, kv head, 16 heads, sequence), "
+         "mfma_f32_16x16x32, logsumexp combine; version=0.1.0";
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal launcher interface between the C ABI (fa_api.cpp) and the kernel
+// translation units.  Arguments have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Lq, Lk, D;
+  float scale;
+  int causal;
+  int bf16;  // 1: bfloat16, 0: float16
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* seqlens;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Lk_max, D;
+  float scale;
+  int num_splits;
+  void* workspace;
+  int bf16;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+
+// Prefill tiling, reported by fa_info().
+constexpr int kFwdWaves = 4;           // wavefronts per workgroup
+constexpr int kFwdRowsPerWave = 32;    // query rows per wavefront
+constexpr int kFwdBM = kFwdWaves * kFwdRowsPerWave;
+constexpr int kDecodeKeysPerStep = 32;
+
+}  // namespace fa

@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs shaped like the pages' attention workloads.
+
+This module only draws numbers; it holds none of the attention arithmetic,
+so both the oracle side and the GPU side of a test may use it.  Everything is
+drawn on the CPU with ``torch.Generator(device="cpu")`` (bitwise reproducible
+anywhere) as float32 N(0,1), in the order Q, K, V, then cast to the workload's
+dtype with round-to-nearest-even.
+
+Workloads (the numbered configurations of the prefill / decode envelope):
+  tiny       B=1  H=2        L=128    D=64  fp16 bidirectional, scale 1/8
+  llama7b    B=4  Hq=Hkv=32  L=4096   D=128 bf16 causal   (Llama-2-7B shape)
+  gqa16k     B=1  Hq=32 Hkv=8 L=16384 D=128 bf16 causal   (long-context GQA)
+  d256       B=2  Hq=Hkv=16  L=4096   D=256 fp16 causal
+  encoder    B=64 H=12       L=512    D=64  fp16 bidirectional, 1% of key rows x8
+  decode     B=128 Hq=32 Hkv=8 D=128 bf16, one query token per sequence,
+             cache lengths uniform on [512, 8192], 8 splits
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Prefill:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    L: int
+    D: int
+    dtype: torch.dtype
+    causal: bool
+    seed: int
+    outlier_frac: float = 0.0  # fraction of key rows scaled by outlier_mult
+    outlier_mult: float = 8.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: 4*D per allowed (query, key) pair per query head."""
+        pairs = self.L * (self.L + 1) // 2 if self.causal else self.L * self.L
+        return 4 * self.D * pairs * self.B * self.Hq
+
+    def hbm_bytes(self) -> int:
+        """Algorithmic bytes: Q, K, V read once; O and lse written once."""
+        e = 2
+        q = self.B * self.L * self.Hq * self.D * e
+        kv = 2 * self.B * self.L * self.Hkv * self.D * e
+        return 2 * q + kv + self.B * self.Hq * self.L * 4
+
+
+@dataclass(frozen=True)
+class Decode:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: torch.dtype
+    len_lo: int
+    len_hi: int  # inclusive
+    num_splits: int
+    seed: int
+    Lk_max: int = field(default=0)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def lmax(self) -> int:
+        return self.Lk_max or self.len_hi
+
+
+PREFILL = {
+    "tiny": Prefill("tiny", 1, 2, 2, 128, 64, torch.float16, False, 1),
+    "llama7b": Prefill("llama7b", 4, 32, 32, 4096, 128, torch.bfloat16, True, 2),
+    "gqa16k": Prefill("gqa16k", 1, 32, 8, 16384, 128, torch.bfloat16, True, 3),
+    "d256": Prefill("d256", 2, 16, 16, 4096, 256, torch.float16, True, 31),
+    "encoder": Prefill("encoder", 64, 12, 12, 512, 64, torch.float16, False, 4, 0.01, 8.0),
+}
+DECODE = {
+    "decode": Decode("decode", 128, 32, 8, 128, torch.bfloat16, 512, 8192, 8, 5),
+}
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def randn_qkv(B, Lq, Lk, Hq, Hkv, D, dtype, seed, *, outlier_frac=0.0, outlier_mult=8.0,
+              q_scale=1.0):
+    """Q [B,Lq,Hq,D], K/V [B,Lk,Hkv,D] on the CPU in ``dtype``.
+
+    Draw order: Q, K, V (float32 N(0,1)); then, if ``outlier_frac`` > 0, a
+    Bernoulli(outlier_frac) mask over key rows (b, j, kv head) whose K vectors
+    are multiplied by ``outlier_mult`` in float32; then the casts.
+    """
+    g = _gen(seed)
+    q = torch.randn((B, Lq, Hq, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Lk, Hkv, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Lk, Hkv, D), generator=g, dtype=torch.float32)
+    if outlier_frac > 0:
+        rows = torch.rand((B, Lk, Hkv), generator=g) < outlier_frac
+        k[rows] *= outlier_mult
+    if q_scale != 1.0:
+        q *= q_scale
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def prefill_inputs(cfg: Prefill):
+    return randn_qkv(cfg.B, cfg.L, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, cfg.dtype, cfg.seed,
+                     outlier_frac=cfg.outlier_frac, outlier_mult=cfg.outlier_mult)
+
+
+def decode_lengths(cfg: Decode) -> torch.Tensor:
+    """Per-sequence cache lengths, uniform on [len_lo, len_hi], int32 [B]."""
+    g = _gen(cfg.seed)
+    return torch.randint(cfg.len_lo, cfg.len_hi + 1, (cfg.B,), generator=g, dtype=torch.int64).to(
+        torch.int32)
+
+
+def decode_inputs(cfg: Decode, *, pad_value=float("nan")):
+    """(q [B,Hq,D], k_cache, v_cache [B,Lk_max,Hkv,D], seqlens int32 [B]) on the CPU.
+
+    Draw order: lengths, Q, then for b = 0..B-1 the K rows then the V rows of
+    sequence b ([len_b, Hkv, D]).  Cache rows past len_b hold ``pad_value``
+    (NaN by default, so that any read of padding shows up in the output).
+    """
+    g = _gen(cfg.seed)
+    lens = torch.randint(cfg.len_lo, cfg.len_hi + 1, (cfg.B,), generator=g, dtype=torch.int64)
+    q = torch.randn((cfg.B, cfg.Hq, cfg.D), generator=g, dtype=torch.float32).to(cfg.dtype)
+    lmax = cfg.lmax
+    kc = torch.full((cfg.B, lmax, cfg.Hkv, cfg.D), pad_value, dtype=cfg.dtype)
+    vc = torch.full((cfg.B, lmax, cfg.Hkv, cfg.D), pad_value, dtype=cfg.dtype)
+    for b in range(cfg.B):
+        n = int(lens[b])
+        kc[b, :n] = torch.randn((n, cfg.Hkv, cfg.D), generator=g, dtype=torch.float32).to(cfg.dtype)
+        vc[b, :n] = torch.randn((n, cfg.Hkv, cfg.D), generator=g, dtype=torch.float32).to(cfg.dtype)
+    return q, kc, vc, lens.to(torch.int32)
+
+
+def decode_bytes(cfg: Decode, lens) -> int:
+    """Algorithmic HBM bytes of one decode step: the K and V rows of every
+    sequence's cache read once, q read once, o and lse written once."""
+    e = 2
+    kv = int(sum(int(x) for x in lens)) * cfg.Hkv * cfg.D * e * 2
+    return kv + 2 * cfg.B * cfg.Hq * cfg.D * e + cfg.B * cfg.Hq * 4
+
+
+def decode_flops(cfg: Decode, lens) -> int:
+    return int(sum(int(x) for x in lens)) * 4 * cfg.Hq * cfg.D

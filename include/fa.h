@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of libfa: exact tiled attention (FlashAttention forward) and
+ * split-KV decode for AMD Instinct MI355X (gfx950).
+ *
+ * Every pointer argument that names a tensor is a DEVICE pointer owned by the
+ * caller; the library keeps no reference to it after the call returns and
+ * never frees it.  All calls are asynchronous: they validate their arguments
+ * on the host, enqueue kernels on `stream` (0 = the null stream) and return.
+ * No call allocates device memory and no call synchronises the device.
+ *
+ * Errors are returned as a status code, never thrown.  On a non-OK status no
+ * kernel has been enqueued (except FA_ERR_HIP, where a launch itself failed),
+ * and fa_last_error() returns a description (thread-local).
+ *
+ * Tensor layouts (all contiguous, row-major, element strides implied):
+ *   q  [B, Lq, Hq, D]      k, v [B, Lk, Hkv, D]     o [B, Lq, Hq, D]
+ *   lse [B, Hq, Lq] float32, natural-log logsumexp of the scaled scores.
+ * This is the [batch, seq, heads, head_dim] layout of the usage example in
+ * "FlashAttention in the CANN ops-transformer library" (ai6s.net), section 4.
+ */
+#ifndef FA_GFX950_FA_H
+#define FA_GFX950_FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad split count, small workspace */
+  FA_ERR_UNSUPPORTED = 2,      /* head_dim not in {64,128,256} or unknown dtype */
+  FA_ERR_HIP = 3               /* a kernel launch failed (text from hipGetErrorString) */
+} fa_status;
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * fa_fwd -- O = softmax(scale * Q K^T + mask) V, computed tile by tile with an
+ * online softmax; the score matrix is never stored.
+ *
+ * Defined by "FlashAttention in the CANN ops-transformer library" (ai6s.net),
+ * section 2 (tiling, per-block running max/sum, blockwise O and L write-back)
+ * and section 4 (arguments q, k, v, softmax_scale, is_causal); GQA head
+ * sharing as in "Enable Flash Attention with llama.cpp" (qualllm.com), FAQ.
+ *
+ *   q, k, v, o  device pointers, elements of type `dtype`, layouts above;
+ *               each must be 16-byte aligned.
+ *   lse         device float32 [B, Hq, Lq]; receives, per query row, the
+ *               logsumexp (natural log) of the scaled scores over the keys
+ *               the row may see.  16-byte aligned.
+ *   B, Lq, Lk   >= 1.   Hq, Hkv >= 1 with Hq % Hkv == 0; query head h reads
+ *               key/value head h / (Hq / Hkv).
+ *   D           head dimension: 64, 128 or 256 (others -> FA_ERR_UNSUPPORTED;
+ *               the head-dim set of the same page, section 5).
+ *   scale       any finite float; scores are scale * q.k.
+ *   causal      0: every query row sees every key (bidirectional, encoder
+ *               use); nonzero: row i sees keys j <= i + (Lk - Lq)
+ *               (bottom-right aligned; the usual lower triangle if Lq == Lk).
+ *               Rows that see no key get o = 0 and lse = -inf.
+ *   dtype       FA_F16 or FA_BF16 for q, k, v and o.  Accumulation is fp32.
+ *   stream      HIP stream to enqueue on.
+ * Returns FA_OK once enqueued.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
+                 fa_dtype dtype, hipStream_t stream);
+
+/*
+ * fa_decode_workspace_size -- bytes of device workspace fa_decode needs for
+ * these sizes: float32 partial outputs [B, Hq, num_splits, D] followed by
+ * float32 partial logsumexps [B, Hq, num_splits].  Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_size(int B, int Hq, int D, int num_splits);
+
+/*
+ * fa_decode -- one query token per sequence attending to its KV cache, split
+ * over key chunks and merged by logsumexp.
+ *
+ * The per-token decode step whose latency the ai6s.net page reports in
+ * section 3; the split-KV form is the split-K decoding backend named by
+ * "5 years, 10K stars: xformers" (cloud.tencent.com).  Chunk c of sequence b
+ * covers keys [c*C_b, min(len_b, (c+1)*C_b)) with C_b = ceil(len_b /
+ * num_splits); each chunk yields a normalised partial output and its
+ * logsumexp, and a second kernel merges them with weights
+ * exp(lse_c - lse_total).
+ *
+ *   q          device [B, Hq, D] (dtype)              16-byte aligned
+ *   k_cache,   device [B, Lk_max, Hkv, D] (dtype); rows j >= seqlens[b] of
+ *   v_cache    sequence b are never read (they may hold anything).
+ *   seqlens    device int32 [B]; sequence b attends to keys 0 .. seqlens[b]-1.
+ *              Values are clamped to [0, Lk_max] on the device; a sequence of
+ *              length 0 gets o = 0 and lse = -inf.
+ *   o          device [B, Hq, D] (dtype);   lse  device float32 [B, Hq].
+ *   num_splits 1 .. 64.
+ *   workspace  device buffer of at least fa_decode_workspace_size(B,Hq,D,
+ *              num_splits) bytes, 16-byte aligned, owned by the caller; its
+ *              contents need not be initialised and are garbage afterwards.
+ *   other arguments as in fa_fwd.
+ * Returns FA_OK once both kernels are enqueued.
+ */
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                    void* o, float* lse, int B, int Hq, int Hkv, int Lk_max, int D, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes,
+                    fa_dtype dtype, hipStream_t stream);
+
+/* Text for the last non-OK status returned on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Static description of the build: target arch, head dims, dtypes, tiles,
+ * version.  Touches no device. */
+const char* fa_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_GFX950_FA_H */

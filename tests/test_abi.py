@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every symbol include/*.h declares, and
+rejects bad arguments on the host before touching the device (CPU only: no
+call here reaches a kernel launch)."""
+
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_fa_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A16 = 1 << 20  # a 16-byte-aligned dummy address; never dereferenced on these paths
+
+
+def declared_functions():
+    names = []
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(hdr).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(fa_[a-z0-9_]+)\s*\(",
+                            src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not _abi.lib_path().exists():
+        pytest.fail(f"{_abi.lib_path()} missing: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    return _abi.load()
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(
+        ["fa_fwd", "fa_decode", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(str(_abi.lib_path()))
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} not exported"
+        assert name in _abi.SIGNATURES, f"{name} has no binding"
+
+
+def test_info_names_target(lib):
+    info = _abi.fa_info()
+    assert "gfx950" in info and "{64,128,256}" in info
+
+
+def fwd(**kw):
+    a = dict(q=A16, k=A16, v=A16, o=A16, lse=A16, B=1, Hq=2, Hkv=1, Lq=8, Lk=8, D=64, scale=0.125,
+             causal=0, dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(q=None), _abi.FA_ERR_INVALID_ARGUMENT, "q is NULL"),
+    (dict(lse=None), _abi.FA_ERR_INVALID_ARGUMENT, "lse is NULL"),
+    (dict(k=A16 + 2), _abi.FA_ERR_INVALID_ARGUMENT, "not 16-byte aligned"),
+    (dict(B=0), _abi.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1"),
+    (dict(Lq=-3), _abi.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1"),
+    (dict(Hq=3, Hkv=2), _abi.FA_ERR_INVALID_ARGUMENT, "not a multiple"),
+    (dict(D=96), _abi.FA_ERR_UNSUPPORTED, "head_dim 96"),
+    (dict(D=32), _abi.FA_ERR_UNSUPPORTED, "head_dim 32"),
+    (dict(dtype=7), _abi.FA_ERR_UNSUPPORTED, "dtype 7"),
+    (dict(scale=float("nan")), _abi.FA_ERR_INVALID_ARGUMENT, "not finite"),
+    (dict(scale=float("inf")), _abi.FA_ERR_INVALID_ARGUMENT, "not finite"),
+    (dict(B=1 << 20, Hq=1 << 10, Hkv=1, Lq=1 << 12), _abi.FA_ERR_INVALID_ARGUMENT, "too large"),
+])
+def test_fwd_rejects(lib, kw, status, text):
+    assert fwd(**kw) == status
+    assert text in _abi.fa_last_error()
+
+
+def dec(**kw):
+    a = dict(q=A16, k=A16, v=A16, seqlens=A16, o=A16, lse=A16, B=2, Hq=8, Hkv=2, Lk_max=64,
+             D=128, scale=0.1, num_splits=8, workspace=A16, workspace_bytes=1 << 30,
+             dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_decode(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(seqlens=None), _abi.FA_ERR_INVALID_ARGUMENT, "seqlens is NULL"),
+    (dict(seqlens=A16 + 2), _abi.FA_ERR_INVALID_ARGUMENT, "4-byte aligned"),
+    (dict(workspace=None), _abi.FA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
+    (dict(workspace_bytes=100), _abi.FA_ERR_INVALID_ARGUMENT, "needs"),
+    (dict(num_splits=0), _abi.FA_ERR_INVALID_ARGUMENT, "num_splits=0"),
+    (dict(num_splits=65), _abi.FA_ERR_INVALID_ARGUMENT, "num_splits=65"),
+    (dict(Hq=6, Hkv=4), _abi.FA_ERR_INVALID_ARGUMENT, "not a multiple"),
+    (dict(D=80), _abi.FA_ERR_UNSUPPORTED, "head_dim 80"),
+    (dict(Lk_max=0), _abi.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1"),
+])
+def test_decode_rejects(lib, kw, status, text):
+    assert dec(**kw) == status
+    assert text in _abi.fa_last_error()
+
+
+def test_workspace_size(lib):
+    assert _abi.fa_decode_workspace_size(128, 32, 128, 8) == 128 * 32 * 8 * (128 + 1) * 4
+    assert _abi.fa_decode_workspace_size(1, 1, 64, 1) == 65 * 4
+    assert _abi.fa_decode_workspace_size(1, 1, 64, 0) == 0
+    assert _abi.fa_decode_workspace_size(0, 1, 64, 1) == 0
+    assert _abi.fa_decode_workspace_size(1, 1, 64, 65) == 0
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("FA_GFX950_LIB", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _abi.load()

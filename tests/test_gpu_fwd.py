@@ -1,0 +1,138 @@
+"""Prefill parity: libfa's fa_fwd (through the C ABI) against the fp64 oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_fa_amd import workloads as W
+from gpu_util import compare, f32, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def run(q, k, v, scale, causal, dev):
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd
+
+    o, lse = flash_attn_fwd(q.to(dev), k.to(dev), v.to(dev), softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check(B, Lq, Lk, Hq, Hkv, D, dtype, causal, seed, gpu, scale=None, q_scale=1.0):
+    scale = f32(scale if scale is not None else 1.0 / np.sqrt(D))
+    q, k, v = W.randn_qkv(B, Lq, Lk, Hq, Hkv, D, dtype, seed, q_scale=q_scale)
+    tag = f"B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} D={D} {str(dtype)[6:]} causal={causal} s={scale:.4g}"
+    say(f"case {tag}")
+    o, lse = run(q, k, v, scale, causal, gpu)
+    o_ref, l_ref = oracle.attention_ref(q, k, v, scale, causal)
+    return compare(o, lse, o_ref, l_ref, tag)
+
+
+RAGGED = [(1, 1), (17, 17), (63, 63), (64, 64), (65, 65), (127, 127), (128, 128), (129, 129),
+          (300, 300), (1000, 1000), (1, 129), (65, 200), (200, 65), (129, 4097)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Lq,Lk", RAGGED, ids=[f"{a}x{b}" for a, b in RAGGED])
+def test_ragged_sweep(Lq, Lk, D, dtype, causal, gpu):
+    check(1, Lq, Lk, 4, 2, D, dtype, causal, seed=Lq * 7919 + Lk + D, gpu=gpu)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_gqa_groups(g, D, gpu):
+    check(2, 257, 257, 8, 8 // g, D, torch.bfloat16, True, seed=31 * g + D, gpu=gpu)
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5, 3.0])
+def test_scale_values(scale, gpu):
+    check(1, 130, 130, 2, 1, 128, torch.bfloat16, True, seed=77, gpu=gpu, scale=scale)
+
+
+def test_large_logits(gpu):
+    """Scores spanning ~+-60: exercises the lazy rescale of the running max."""
+    check(1, 700, 700, 2, 2, 64, torch.float16, False, seed=78, gpu=gpu, q_scale=8.0)
+    check(1, 700, 700, 2, 2, 128, torch.bfloat16, True, seed=79, gpu=gpu, q_scale=8.0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "encoder"])
+def test_config_full(name, gpu):
+    cfg = W.PREFILL[name]
+    say(f"config {name}: {cfg}")
+    q, k, v = W.prefill_inputs(cfg)
+    o, lse = run(q, k, v, f32(cfg.scale), cfg.causal, gpu)
+    o_ref, l_ref = oracle.attention_ref(q, k, v, f32(cfg.scale), cfg.causal)
+    compare(o, lse, o_ref, l_ref, name)
+
+
+@pytest.mark.parametrize("name,nheads", [("llama7b", 3), ("gqa16k", 2), ("d256", 3)])
+def test_config_full_size_sampled(name, nheads, gpu):
+    """Full-size launch (the shape the benchmark times); the oracle computes
+    a few whole (batch, head) slices, including the first and the last."""
+    cfg = W.PREFILL[name]
+    say(f"config {name}: {cfg}")
+    q, k, v = W.prefill_inputs(cfg)
+    o, lse = run(q, k, v, f32(cfg.scale), cfg.causal, gpu)
+    rs = np.random.default_rng(cfg.seed)
+    heads = {(0, 0), (cfg.B - 1, cfg.Hq - 1)}
+    while len(heads) < nheads:
+        heads.add((int(rs.integers(cfg.B)), int(rs.integers(cfg.Hq))))
+    o_ref, l_ref = oracle.attention_ref(q, k, v, f32(cfg.scale), cfg.causal, heads=sorted(heads))
+    compare(o, lse, o_ref, l_ref, f"{name} heads={sorted(heads)}")
+
+
+def test_causal_row0_is_exact(gpu):
+    """Row 0 sees only key 0: P = 1 exactly, so O_0 = V[0] bit for bit and
+    lse_0 = scale * q_0.k_0."""
+    B, L, H, D = 2, 200, 4, 128
+    q, k, v = W.randn_qkv(B, L, L, H, H, D, torch.bfloat16, 90)
+    o, lse = run(q, k, v, f32(D ** -0.5), True, gpu)
+    assert torch.equal(o[:, 0], v[:, 0])
+    s00 = f32(D ** -0.5) * (to64(q[:, 0]) * to64(k[:, 0])).sum(-1)  # [B, H]
+    assert np.max(np.abs(lse[:, :, 0].double().numpy() - s00)) < 1e-4
+
+
+def test_uniform_queries_give_prefix_means(gpu):
+    B, L, H, D = 1, 333, 2, 64
+    _, k, v = W.randn_qkv(B, L, L, H, H, D, torch.float16, 91)
+    q = torch.zeros((B, L, H, D), dtype=torch.float16)
+    o, lse = run(q, k, v, 0.125, True, gpu)
+    means = np.cumsum(to64(v)[0], axis=0) / np.arange(1, L + 1)[:, None, None]
+    assert np.max(np.abs(to64(o)[0] - means)) < 2e-2
+    assert np.max(np.abs(lse[0].double().numpy() - np.log(np.arange(1, L + 1))[None])) < 1e-3
+
+
+def test_constant_values(gpu):
+    B, L, H, D = 1, 257, 2, 128
+    q, k, _ = W.randn_qkv(B, L, L, H, H, D, torch.bfloat16, 92, q_scale=4.0)
+    c = torch.linspace(-3, 3, D).to(torch.bfloat16)
+    v = c.expand(B, L, H, D).contiguous()
+    o, _ = run(q, k, v, D ** -0.5, True, gpu)
+    assert np.max(np.abs(to64(o) - to64(c)[None, None, None, :])) < 2e-2
+
+
+def test_deterministic(gpu):
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd
+
+    q, k, v = (t.to(gpu) for t in W.randn_qkv(2, 1000, 1000, 8, 2, 128, torch.bfloat16, 93))
+    outs = [flash_attn_fwd(q, k, v, causal=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_errors_are_raised(gpu):
+    from exact_tiled_attention_fa_amd.attention import FAError, flash_attn_fwd
+
+    q = torch.zeros((1, 8, 2, 96), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(FAError, match="FA_ERR_UNSUPPORTED"):
+        flash_attn_fwd(q, q, q)
+    q = torch.zeros((1, 8, 3, 64), dtype=torch.bfloat16, device=gpu)
+    k = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(FAError, match="FA_ERR_INVALID_ARGUMENT"):
+        flash_attn_fwd(q, k, k)
