@@ -69,6 +69,41 @@ template <> struct Ops<f16_t> {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+#define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define FA_GLOBAL(T, p) ((__attribute__((address_space(1))) T*)(p))
+
+// Asynchronous 16-byte HBM -> LDS copy (global_load_lds_dwordx4).  `lds` must
+// be the same for every lane of the wave: lane l's 16 bytes land at lds + 16*l.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(FA_GLOBAL(void, g), FA_LDS(void, lds), 16, 0, 0);
+}
+
+// Wait until this wave's vector-memory loads (including LDS-direct ones) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ds_read_b64_tr_b16.  Within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte chunk addressed by lane 4k + i/4, for k = 0..3.  With
+// lane j of the group pointing at row (r0 + j/4), columns c0 + 4*(j%4) .. +3
+// of a row-major 16-bit matrix, lane i gets column c0 + i of rows r0..r0+3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(i16x4, p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// v_permlane32_swap(x, x) gives (x of lane l%32, x of lane l%32 + 32) in every
+// lane, so a reduction across the two wave halves is one swap and one op.
+__device__ __forceinline__ float max_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Value held by lane (lane ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 __device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16); }

@@ -12,25 +12,33 @@
 // wavefronts so each row's statistics stay in one wavefront's registers.
 //
 // gfx950 mapping (one workgroup = 4 wave64 = 128 query rows):
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: A = K rows from LDS,
-//     B = Q^T held in registers for the whole kernel.  The accumulator puts
-//     one query per lane column (lane % 32) and 16 of the 32 keys of a block
-//     in that lane, so a row's max/sum need only one cross-half exchange.
+//   * K and V tiles of BN keys stream HBM -> LDS with global_load_lds_dwordx4
+//     (no VGPR round trip), double-buffered: the copy of tile t+1 runs while
+//     tile t is computed; one barrier per tile.  Rows are stored row-major
+//     with their 16-byte chunks XOR-swizzled by row so that the MFMA operand
+//     reads below hit distinct LDS banks.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: A = K rows from LDS
+//     (ds_read_b128), B = Q^T held in registers for the whole kernel.  The
+//     accumulator holds one query per lane column (lane % 32) and 16 of a
+//     32-key block's scores per lane, so a row's max and sum need one
+//     cross-half exchange (v_permlane32_swap).
 //   * O^T += V^T P^T with the same MFMA: B = P^T straight from the score
-//     registers (rounded to the input type), A = V^T read from an LDS tile
-//     that was transposed on the way in.  The output accumulator keeps the
-//     query in the lane, so rescaling it is lane-local.
-//   * Keys of the transposed V tile are stored at permuted positions (4-key
-//     groups with their two low group bits swapped) so that the eight keys a
-//     lane needs for one MFMA k-step are 16 contiguous bytes.
+//     registers (rounded to the input type), A = V^T read from the row-major
+//     V tile with ds_read_b64_tr_b16, which hands each lane one head-dim
+//     column of four consecutive keys.  The output accumulator keeps the
+//     query in the lane, so its rescale is lane-local.
 //   * Causal: KV tiles entirely above the diagonal are never loaded; only
 //     tiles that straddle the diagonal or the ragged key tail take the masked
 //     path.  Workgroups are issued heaviest query tile first.
-//   * Lazy rescaling: the reference max of a row is only moved when a new
-//     score exceeds it by more than 2^8 in the exponent, so the accumulator
-//     rescale (D/2 multiplies per lane) runs rarely; probabilities stay
-//     <= 256, well inside bf16/fp16 range, and the final O = acc / l and
-//     lse = m_ref + log(l) are unchanged up to rounding.
+//   * Lazy rescaling: a row's reference max moves only when a new score
+//     exceeds it by more than 2^8 in the exponent, so the accumulator rescale
+//     (D/2 multiplies per lane) is rare; probabilities stay <= 256, inside
+//     bf16/fp16 range, and O = acc / l and lse = m_ref + log(l) are unchanged
+//     up to rounding.
+//   * The output tile is staged through LDS so each row is written to HBM as
+//     full contiguous 16-byte-per-lane stores.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -39,18 +47,49 @@ namespace {
 
 constexpr int kNT = kFwdWaves * 64;
 
-template <typename T, int D, int BN, bool CAUSAL>
+// Keys per KV tile.  The pipelined loop keeps two score tiles, the packed
+// probabilities, the output accumulator and Q in registers; at D >= 128 a
+// 32-key tile keeps that within 256 VGPRs (two waves per SIMD).
+#ifndef FA_FWD_BN_D64
+#define FA_FWD_BN_D64 64
+#endif
+#ifndef FA_FWD_BN_D128
+#define FA_FWD_BN_D128 32
+#endif
+template <int D> struct FwdTile { static constexpr int BN = FA_FWD_BN_D64; };
+template <> struct FwdTile<128> { static constexpr int BN = FA_FWD_BN_D128; };
+template <> struct FwdTile<256> { static constexpr int BN = 32; };
+
+// XOR applied to a row's 16-byte chunk index in the K tile (conflict-free
+// ds_read_b128 of 16 consecutive rows at one logical chunk) ...
+template <int D> __device__ __forceinline__ int swz_k(int r) {
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// ... and in the V tile (conflict-free transpose reads of 4 consecutive rows).
+template <int D> __device__ __forceinline__ int swz_v(int r) {
+  return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kNT, (D <= 128 ? 2 : 1))
 void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int B, int Hq, int Hkv, int Lq, int Lk,
                 float scale2, float thr, uint32_t qxor) {
   constexpr int BM = kFwdBM;
-  constexpr int KP = D + 8;   // K tile row pitch (elements): +16 bytes against bank conflicts
-  constexpr int VP = BN + 8;  // V^T tile row pitch (elements)
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VP];
+  constexpr int BN = FwdTile<D>::BN;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE = BN * D;               // elements per K or V tile
+  constexpr int NLOAD = BN * CPR / kNT;      // LDS-direct loads per thread per tile (each of K, V)
+  static_assert(BN % 32 == 0 && D % 32 == 0 && (BN * CPR) % kNT == 0, "tile shape");
+  static_assert(kFwdWaves == 4 && 32 * D <= TILE, "output staging uses one tile array per wave");
+  // Two stages of K and V tiles.  Four distinct arrays (not slices of one)
+  // let the compiler see that reading one stage does not alias the
+  // LDS-direct copy into the other, so it inserts no wait between them.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -77,6 +116,54 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* Kb = K + (long)b * Lk * kstride + (long)kvh * D;
   const uint16_t* Vb = V + (long)b * Lk * kstride + (long)kvh * D;
 
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, min(q0 + BM, Lq) + shift);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  // Loader: load i of this thread fills 16-byte chunk position P of the tile
+  // (row P / CPR, stored chunk P % CPR holding logical chunk (P % CPR) ^ swz).
+  // ldk/ldv are the element offsets of that chunk from the tile's first row.
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform copy for LDS bases
+  int ldk[NLOAD], ldv[NLOAD];
+#pragma unroll
+  for (int i = 0; i < NLOAD; ++i) {
+    const int P = (i * kFwdWaves + wu) * 64 + lane;
+    const int r = P / CPR, pc = P % CPR;
+    ldk[i] = r * (int)kstride + 8 * (pc ^ swz_k<D>(r));
+    ldv[i] = r * (int)kstride + 8 * (pc ^ swz_v<D>(r));
+  }
+  // Rows past Lk (only in the last tile) are redirected to row Lk-1: any
+  // finite row will do, their scores are masked.
+  auto clamp_off = [&](int i, int j0, int off) {
+    const int r = ((i * kFwdWaves + wu) * 64 + lane) / CPR;
+    return off + (min(j0 + r, Lk - 1) - (j0 + r)) * (int)kstride;
+  };
+  auto issue_k = [&](int t, uint16_t* dK) {
+    const int j0 = t * BN;
+    const uint16_t* base = Kb + (long)j0 * kstride;
+    const bool ragged = j0 + BN > Lk;
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i)
+      load_lds16(base + (ragged ? clamp_off(i, j0, ldk[i]) : ldk[i]),
+                 dK + (i * kFwdWaves + wu) * 512);
+  };
+  auto issue_v = [&](int t, uint16_t* dV) {
+    const int j0 = t * BN;
+    const uint16_t* base = Vb + (long)j0 * kstride;
+    const bool ragged = j0 + BN > Lk;
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i)
+      load_lds16(base + (ragged ? clamp_off(i, j0, ldv[i]) : ldv[i]),
+                 dV + (i * kFwdWaves + wu) * 512);
+  };
+  // K runs one tile ahead of V: tile t's scores are computed while tile t-1's
+  // probabilities meet V.
+  if (ntiles > 0) {
+    issue_k(0, sK0);
+    issue_v(0, sV0);
+  }
+  if (ntiles > 1) issue_k(1, sK1);
+
   // Q^T operand: lane holds query `qrow`, 8 dims per 16-dim k-step.
   u32x4 qf[D / 16];
 #pragma unroll
@@ -89,9 +176,20 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   }
 
-  int kend = Lk;
-  if (CAUSAL) kend = min(Lk, min(q0 + BM, Lq) + shift);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // Per-lane LDS element offsets of the MFMA operand reads.
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * D + 8 * ((2 * ks + hf) ^ swz_k<D>(l32));
+  // V^T read for k-step t, half r, head-dim block db: row 16t + 8r + 4hf + (lane%16)/4,
+  // columns 32db + 16*((lane/16)%2) + 4*(lane%4) .. +3.  swz_v depends only on the lane here.
+  const int vrow = 4 * hf + ((lane & 15) >> 2);
+  int voff[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    voff[db] = vrow * D + 8 * ((col >> 3) ^ swz_v<D>(vrow)) + (col & 7);
+  }
+
   const bool wave_live = qw0 < Lq;
   const int qw_last = min(qw0 + kFwdRowsPerWave - 1, Lq - 1);
   const int wave_kmax = CAUSAL ? min(Lk - 1, qw_last + shift) : Lk - 1;
@@ -101,62 +199,39 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
   float m_ref = -INFINITY;  // reference max (raw score units) of this lane's row
-  float l_part = 0.f;       // this lane's share of the row sum (relative to m_ref)
+  float l_part = 0.f;       // this lane's half of the row sum (relative to m_ref)
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * BN;
-    __syncthreads();  // every wave is done reading the previous tile
-    // K tile, row-major [BN][D]; rows past Lk are zero.
-    for (int p = tid; p < BN * (D / 8); p += kNT) {
-      const int r = p / (D / 8), c = p - r * (D / 8);
-      u32x4 x = (u32x4){0u, 0u, 0u, 0u};
-      if (j0 + r < Lk) x = load16(Kb + (long)(j0 + r) * kstride + 8 * c);
-      store16(sK + r * KP + 8 * c, x);
-    }
-    // V tile, transposed to [D][BN] with permuted key positions.
-    for (int p = tid; p < (BN / 4) * (D / 8); p += kNT) {
-      const int g = p % (BN / 4), c = p / (BN / 4);
-      u32x4 x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + 4 * g + i;
-        x[i] = (j < Lk) ? load16(Vb + (long)j * kstride + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
-      }
-      const int pg = (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int word = e >> 1;
-        const int sh = (e & 1) * 16;
-        const uint32_t k0 = (x[0][word] >> sh) & 0xffffu, k1 = (x[1][word] >> sh) & 0xffffu;
-        const uint32_t k2 = (x[2][word] >> sh) & 0xffffu, k3 = (x[3][word] >> sh) & 0xffffu;
-        u32x2 val = {k0 | (k1 << 16), k2 | (k3 << 16)};
-        *reinterpret_cast<u32x2*>(sV + (8 * c + e) * VP + 4 * pg) = val;
-      }
-    }
-    __syncthreads();
-    if (!wave_live || j0 > wave_kmax) continue;  // whole tile masked for this wave
+  // Tiles with index <= last_live hold at least one key some row of this wave sees.
+  const int last_live = wave_live && wave_kmax >= 0 ? wave_kmax / BN : -1;
 
-    // S^T = K Q^T for BN keys x 32 queries.
-    f32x16 s[BN / 32];
+  // S^T = K Q^T for BN keys x 32 queries (raw scores).
+  auto scores = [&](f32x16 (&s)[BN / 32], const uint16_t* sK) {
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
       s[kb] = (f32x16){};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + (32 * kb + l32) * KP + 16 * ks + 8 * hf);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + 32 * kb * D + koff[ks]);
         s[kb] = Ops<T>::mfma32(a, qf[ks], s[kb]);
       }
     }
+  };
 
-    const bool need_mask = (j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > qw0 + shift);
+  // Folds tile t's row max into the reference max and rescales the
+  // accumulator if it moved.  With MASK, first sets the scores of keys the row
+  // may not see to -inf (only tiles crossing the diagonal or the key tail).
+  auto fold = [&](f32x16 (&s)[BN / 32], int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int j0 = t * BN;
     float mx = -INFINITY;
-    if (need_mask) {
+    if (MASK && ((j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > qw0 + shift))) {
+      // key j0 + 32kb + 8(r/4) + 4hf + r%4 is visible iff it is <= row_kmax
+      const int lim = row_kmax - j0 - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key > row_kmax) s[kb][r] = -INFINITY;
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
           mx = fmaxf(mx, s[kb][r]);
         }
     } else {
@@ -165,10 +240,12 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     }
-    mx = fmaxf(mx, xor32(mx));
-
+    mx = max_halves(mx);
     const bool upd = mx > m_ref + thr;
-    if (__builtin_amdgcn_ballot_w64(upd)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(upd) != 0, 0)) {
+      // Rare: keep it a real branch (the marker stops it being turned into
+      // unconditional multiplies of the whole accumulator).
+      asm volatile("" ::: "memory");
       const float m_new = upd ? mx : m_ref;
       const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast((m_ref - m_new) * scale2);
       l_part *= alpha;
@@ -176,72 +253,138 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       m_ref = m_new;
     }
-    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * scale2;
+  };
 
-    // P = exp2(s*scale2 - m*scale2).  The MFMA takes P rounded to T; the row
-    // sum adds the unrounded fp32 values, so lse carries no 16-bit rounding
-    // (summing the rounded values would shift ln(l) by up to 2^-9 for rows
-    // with few keys).
-    uint32_t pk[BN / 32][8];
+  // P = exp2(s*scale2 - m*scale2) for a folded tile, rounded to T and packed
+  // as the B operand of the PV MFMA.  Masked scores are -inf and give exactly
+  // 0 (scale2 > 0, mb finite).  The row sum adds the unrounded fp32 values,
+  // so lse carries no 16-bit rounding (summing the rounded values would shift
+  // ln(l) by up to 2^-9 for rows with few keys).
+  auto make_p = [&](const f32x16 (&s)[BN / 32], uint32_t (&pk)[BN / 32][8]) {
+    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * scale2;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float p0 = exp2_fast(__builtin_fmaf(s[kb][2 * j], scale2, -mb));
-        float p1 = exp2_fast(__builtin_fmaf(s[kb][2 * j + 1], scale2, -mb));
-        if (need_mask) {
-          p0 = (s[kb][2 * j] == -INFINITY) ? 0.f : p0;
-          p1 = (s[kb][2 * j + 1] == -INFINITY) ? 0.f : p1;
-        }
+        const float p0 = exp2_fast(__builtin_fmaf(s[kb][2 * j], scale2, -mb));
+        const float p1 = exp2_fast(__builtin_fmaf(s[kb][2 * j + 1], scale2, -mb));
         pk[kb][j] = Ops<T>::pack2(p0, p1);
         l_part += p0 + p1;
       }
-
-    // O^T += V^T P^T, 16 keys per MFMA k-step.
+  };
+  // O^T += V^T P^T, 16 keys per MFMA k-step (slots 4r+k <-> key 16t+8r+4hf+k).
+  auto pv = [&](const uint32_t (&pk)[BN / 32][8], const uint16_t* sV) {
 #pragma unroll
     for (int ts = 0; ts < BN / 16; ++ts) {
       const int kb = ts >> 1, c = ts & 1;
       const u32x4 bop = {pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]};
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sV + (32 * db + l32) * VP + 16 * ts + 8 * hf);
+        const u32x2 lo = lds_read_tr16(sV + 16 * ts * D + voff[db]);
+        const u32x2 hi = lds_read_tr16(sV + (16 * ts + 8) * D + voff[db]);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         acc[db] = Ops<T>::mfma32(a, bop, acc[db]);
       }
     }
+  };
+
+  // One pipeline step for tile t: its scores sc are folded already, K(t+1)
+  // sits in kn and V(t) in vc.  Refills the buffers of K(t) and V(t-1) with
+  // K(t+2) and V(t+1), then computes P(t), S(t+1) and P(t) V(t).  In the
+  // main phase (TAIL false) tiles t and t+1 are fully visible to every row of
+  // the workgroup, so nothing is masked or skipped.
+  auto step = [&](int t, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32], const uint16_t* kn,
+                  uint16_t* kfree, const uint16_t* vc, uint16_t* vn, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    wait_vmem();
+    __syncthreads();  // K(t+1), V(t) have landed; nobody reads K(t) or V(t-1) any more
+    if (t + 2 < ntiles) issue_k(t + 2, kfree);
+    if (t + 1 < ntiles) issue_v(t + 1, vn);
+    if (TAIL && t > last_live) return;  // every key of tile t is hidden from this wave
+    uint32_t pk[BN / 32][8];
+    make_p(sc, pk);
+    if (!TAIL || t + 1 <= last_live) {
+      scores(sn, kn);
+      pv(pk, vc);
+      fold(sn, t + 1, std::integral_constant<bool, TAIL>{});
+    } else {
+      pv(pk, vc);
+    }
+  };
+
+  // Tiles [0, n_main) are seen whole by every row of the workgroup.
+  const int kall = CAUSAL ? min(Lk, q0 + shift + 1) : Lk;
+  const int n_main = kall > 0 ? min(ntiles, kall / BN) : 0;
+  using Main = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+
+  f32x16 sA[BN / 32], sB[BN / 32];
+  wait_vmem();
+  __syncthreads();  // K(0), V(0), K(1) have landed
+  if (0 <= last_live && ntiles > 0) {
+    scores(sA, sK0);
+    fold(sA, 0, Tail{});
+  }
+  // Both phases walk tiles in pairs from an even index, so the score arrays
+  // and stage buffers are in the same roles at every loop head.
+  int t = 0;
+  // Main phase: step t runs unmasked when tiles t and t+1 are both whole.
+  while (t + 2 < n_main) {
+    step(t, sA, sB, sK1, sK0, sV0, sV1, Main{});
+    step(t + 1, sB, sA, sK0, sK1, sV1, sV0, Main{});
+    t += 2;
+  }
+  // Tail phase: masked or partly skipped tiles (and the last whole ones).
+  while (t < ntiles) {
+    step(t, sA, sB, sK1, sK0, sV0, sV1, Tail{});
+    if (t + 1 >= ntiles) break;
+    step(t + 1, sB, sA, sK0, sK1, sV1, sV0, Tail{});
+    t += 2;
   }
 
-  // Epilogue: full row sum, O = acc / l, lse = ln(2) * (m*scale2 + log2 l).
-  const float l = l_part + xor32(l_part);
-  if (qrow < Lq) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* Orow = O + ((long)b * Lq + qrow) * qstride + (long)h * D;
+  // Epilogue: full row sum, O = acc / l staged through LDS (wave w uses one
+  // stage array, rows [32][D] with 16-byte chunks XOR-swizzled by row), then
+  // written as whole rows; lse = ln2 * (m*scale2 + log2 l).
+  const float l = sum_halves(l_part);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  constexpr int OSW = CPR < 16 ? CPR - 1 : 15;
+  __syncthreads();  // all waves are done with the K/V tiles
+  uint16_t* so = (w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d = 32 * db + 8 * a4 + 4 * hf;
-        u32x2 val = {Ops<T>::pack2(acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv),
-                     Ops<T>::pack2(acc[db][4 * a4 + 2] * inv, acc[db][4 * a4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(Orow + d) = val;
-      }
-    if (hf == 0) {
-      LSE[(long)bh * Lq + qrow] =
-          l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = 32 * db + 8 * a4 + 4 * hf;
+      u32x2 val = {Ops<T>::pack2(acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv),
+                   Ops<T>::pack2(acc[db][4 * a4 + 2] * inv, acc[db][4 * a4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(so + l32 * D + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
     }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int p = lane + 64 * i;
+    const int row = p / CPR, c = p % CPR;
+    const int q = qw0 + row;
+    if (q < Lq)
+      store16(O + ((long)b * Lq + q) * qstride + (long)h * D + 8 * c,
+              *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))));
   }
+  if (hf == 0 && qrow < Lq)
+    LSE[(long)bh * Lq + qrow] = l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BN = 64;
   const int nqt = (a.Lq + kFwdBM - 1) / kFwdBM;
   const long nblocks = (long)nqt * a.B * a.Hq;
   const float s = a.scale;
-  const float scale2 = fabsf(s) * kLog2e;
+  // |scale| * log2(e), kept >= 1e-30 so that masked (-inf) scores always give
+  // probability 0; for scale 0 this changes no result beyond 1e-30 relative.
+  const float scale2 = fmaxf(fabsf(s) * kLog2e, 1e-30f);
   // Rescale threshold of 8 (log2 units) expressed in raw score units.
-  const float thr = scale2 > 0.f ? 8.f / scale2 : 1e30f;
+  const float thr = 8.f / scale2;
   const uint32_t qxor = (s < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_kernel<T, D, BN, CAUSAL>), dim3((unsigned)nblocks), dim3(kNT), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)nblocks), dim3(kNT), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lq, a.Lk, scale2, thr, qxor);
   return hipGetLastError();
