@@ -37,6 +37,12 @@ template <> struct Ops<bf16_t> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  // D(16x16) += A(16x16) * B(16x16); 4 elements of 16 bits per lane.
+  static __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
   // Two floats -> two bf16 (RNE) in one dword, `lo` in the low half.
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     bf16x2 v = {(__bf16)lo, (__bf16)hi};
@@ -54,6 +60,11 @@ template <> struct Ops<f16_t> {
   static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f16x2 v = {(_Float16)lo, (_Float16)hi};
@@ -78,8 +89,13 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(FA_GLOBAL(void, g), FA_LDS(void, lds), 16, 0, 0);
 }
 
+// s_waitcnt immediate that waits until at most n (< 64) of this wave's
+// vector-memory operations are outstanding (vmcnt is split over bits 3:0 and
+// 15:14; expcnt and lgkmcnt are left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // Wait until this wave's vector-memory loads (including LDS-direct ones) are done.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
 
 // ds_read_b64_tr_b16.  Within each group of 16 lanes, lane i receives element
 // (i % 4) of the 8-byte chunk addressed by lane 4k + i/4, for k = 0..3.  With

@@ -42,6 +42,6 @@ size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 constexpr int kFwdWaves = 4;           // wavefronts per workgroup
 constexpr int kFwdRowsPerWave = 32;    // query rows per wavefront
 constexpr int kFwdBM = kFwdWaves * kFwdRowsPerWave;
-constexpr int kDecodeKeysPerStep = 32;
+constexpr int kDecodeKeysPerStep = 16;
 
 }  // namespace fa
