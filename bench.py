@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
     p.add_argument("--all-configs", action="store_true",
                    help="also print one extra JSON line per prefill workload")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn two rocprofv3 --pmc runs of this script with "
+                        "--with-copy (FETCH_SIZE, then WRITE_SIZE) into profiles/traffic.json")
     return p.parse_args()
 
 
@@ -73,6 +76,56 @@ def traffic_for(kernel: str, digest: str):
     except (OSError, ValueError):
         pass
     return None
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
+    """HBM bytes per launch of the prefill and decode kernels from rocprofv3
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same
+    counter reads for a plain device copy of copy_mib MiB (reads and writes
+    exactly copy_mib MiB)."""
+    import csv
+    import glob
+    import statistics
+
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter:
+                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    def med(rows, pred):
+        v = [x for _, n, x in rows if pred(n)]
+        return statistics.median(v) if v else None
+
+    is_copy = lambda n: "copybuffer" in n.lower()  # the runtime's device-to-device copy kernel
+    is_fwd = lambda n: "fwd_kernel<fa::bf16_t, 128, true>" in n
+    is_split = lambda n: "decode_split_kernel<fa::bf16_t, 128>" in n
+    is_comb = lambda n: "decode_combine_kernel<fa::bf16_t, 128>" in n
+    fr, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    kib = copy_mib * 1024.0
+    # only the calibration copies (the run also holds small input uploads)
+    fr = [r for r in fr if not is_copy(r[1]) or r[2] > kib / 16]
+    wr = [r for r in wr if not is_copy(r[1]) or r[2] > kib / 16]
+    ff = kib / med(fr, is_copy)
+    fw = kib / med(wr, is_copy)
+    out = {"_about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                     "dispatch, median over dispatches), each scaled by the factor that makes a "
+                     f"plain {copy_mib} MiB device copy read and write exactly {copy_mib} MiB.",
+           "copy_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
+    f_k, w_k = med(fr, is_fwd), med(wr, is_fwd)
+    if f_k is not None and w_k is not None:
+        out["fwd_kernel"] = {"source_digest": source_digest(["fa_fwd.hip", "fa_common.hpp"]),
+                             "fetch_kib": f_k, "write_kib": w_k,
+                             "bytes_per_launch": int((f_k * ff + w_k * fw) * 1024)}
+    parts = [(med(fr, p), med(wr, p)) for p in (is_split, is_comb)]
+    if all(a is not None and b is not None for a, b in parts):
+        out["decode"] = {"source_digest": source_digest(["fa_decode.hip", "fa_common.hpp"]),
+                         "fetch_kib": sum(a for a, _ in parts), "write_kib": sum(b for _, b in parts),
+                         "bytes_per_launch": int(sum(a * ff + b * fw for a, b in parts) * 1024)}
+    return out
 
 
 def cpu_baseline_prefill(cfg, q, k, v, scale, target_s):
@@ -114,6 +167,13 @@ def cpu_baseline_decode(cfg, q, kc, vc, lens, scale, nseq=16):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        t = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.with_copy or 1024)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
                  "(run with --gpus 1).")

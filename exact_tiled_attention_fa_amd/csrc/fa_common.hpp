@@ -94,6 +94,12 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
 // 15:14; expcnt and lgkmcnt are left at their maxima).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
+// Same copy from a wave-uniform base plus a 32-bit per-lane byte offset, so
+// the load can use scalar-base addressing with no per-lane 64-bit math.
+__device__ __forceinline__ void load_lds16_off(const void* base, uint32_t off_bytes, void* lds) {
+  load_lds16(static_cast<const char*>(base) + off_bytes, lds);
+}
+
 // Wait until this wave's vector-memory loads (including LDS-direct ones) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
 

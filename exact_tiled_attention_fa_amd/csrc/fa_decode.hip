@@ -187,13 +187,17 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
   u32x4 kA[D / 32], kB[D / 32], vA[NVL], vB[NVL];
   kload(w, kA);  // (a wave with no step reads the chunk's last row, unused)
   vload(w, vA);
+  // The scheduling barriers keep each request ahead of the wait for the step
+  // being computed, so two steps are in flight while that wait lasts.
   for (int i = 0; i < my_steps; i += 2) {
     kload(w + kDW * (i + 1), kB);
     vload(w + kDW * (i + 1), vB);
+    __builtin_amdgcn_sched_barrier(0);
     compute(w + kDW * i, kA, vA);
     if (i + 1 >= my_steps) break;
     kload(w + kDW * (i + 2), kA);
     vload(w + kDW * (i + 2), vA);
+    __builtin_amdgcn_sched_barrier(0);
     compute(w + kDW * (i + 1), kB, vB);
   }
 

@@ -46,6 +46,7 @@ namespace fa {
 namespace {
 
 constexpr int kNT = kFwdWaves * 64;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 
 // Keys per KV tile.  The pipelined loop keeps two score tiles, the packed
 // probabilities, the output accumulator and Q in registers; at D >= 128 a
@@ -82,7 +83,9 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int TILE = BN * D;               // elements per K or V tile
   constexpr int NLOAD = BN * CPR / kNT;      // LDS-direct loads per thread per tile (each of K, V)
   static_assert(BN % 32 == 0 && D % 32 == 0 && (BN * CPR) % kNT == 0, "tile shape");
-  static_assert(kFwdWaves == 4 && 32 * D <= TILE, "output staging uses one tile array per wave");
+  // The output is staged through LDS (one tile array per wave) when four
+  // waves' 32 x D tiles fit; otherwise it is stored straight from registers.
+  constexpr bool kStageO = kFwdWaves == 4 && 32 * D <= TILE;
   // Two stages of K and V tiles.  Four distinct arrays (not slices of one)
   // let the compiler see that reading one stage does not alias the
   // LDS-direct copy into the other, so it inserts no wait between them.
@@ -97,11 +100,18 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
+  // Block -> work item.  The work list is ordered (batch, query head, query
+  // tile heaviest first); query heads that share a K/V head are adjacent.
+  // Blocks are dealt to the XCDs round-robin (block i runs on XCD i % 8), so
+  // XCD x is given the x-th contiguous slice of the list: at any moment each
+  // XCD works on a few heads, whose K/V tiles then stay in its own L2.
   const int nqt = (Lq + BM - 1) / BM;
-  const int BH = B * Hq;
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles are dispatched first
+  const int N = nqt * B * Hq;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int item = xcd * (N / kXcds) + min(xcd, N % kXcds) + slot;
+  const int bh = item / nqt;
+  int qt = item - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int kvh = h / (Hq / Hkv);
@@ -122,40 +132,36 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // Loader: load i of this thread fills 16-byte chunk position P of the tile
   // (row P / CPR, stored chunk P % CPR holding logical chunk (P % CPR) ^ swz).
-  // ldk/ldv are the element offsets of that chunk from the tile's first row.
+  // ldk/ldv are that chunk's byte offsets from the tile's first row.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform copy for LDS bases
-  int ldk[NLOAD], ldv[NLOAD];
+  uint32_t ldk[NLOAD], ldv[NLOAD];
 #pragma unroll
   for (int i = 0; i < NLOAD; ++i) {
     const int P = (i * kFwdWaves + wu) * 64 + lane;
     const int r = P / CPR, pc = P % CPR;
-    ldk[i] = r * (int)kstride + 8 * (pc ^ swz_k<D>(r));
-    ldv[i] = r * (int)kstride + 8 * (pc ^ swz_v<D>(r));
+    ldk[i] = 2u * (uint32_t)(r * (int)kstride + 8 * (pc ^ swz_k<D>(r)));
+    ldv[i] = 2u * (uint32_t)(r * (int)kstride + 8 * (pc ^ swz_v<D>(r)));
   }
   // Rows past Lk (only in the last tile) are redirected to row Lk-1: any
   // finite row will do, their scores are masked.
-  auto clamp_off = [&](int i, int j0, int off) {
+  auto clamp_off = [&](int i, int j0, uint32_t off) {
     const int r = ((i * kFwdWaves + wu) * 64 + lane) / CPR;
-    return off + (min(j0 + r, Lk - 1) - (j0 + r)) * (int)kstride;
+    return off - 2u * (uint32_t)(((j0 + r) - min(j0 + r, Lk - 1)) * (int)kstride);
   };
-  auto issue_k = [&](int t, uint16_t* dK) {
+  auto issue = [&](const uint16_t* src, const uint32_t (&ld)[NLOAD], int t, uint16_t* dst) {
     const int j0 = t * BN;
-    const uint16_t* base = Kb + (long)j0 * kstride;
-    const bool ragged = j0 + BN > Lk;
+    const uint16_t* base = src + (long)j0 * kstride;  // wave-uniform
+    if (j0 + BN <= Lk) {
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i)
-      load_lds16(base + (ragged ? clamp_off(i, j0, ldk[i]) : ldk[i]),
-                 dK + (i * kFwdWaves + wu) * 512);
-  };
-  auto issue_v = [&](int t, uint16_t* dV) {
-    const int j0 = t * BN;
-    const uint16_t* base = Vb + (long)j0 * kstride;
-    const bool ragged = j0 + BN > Lk;
+      for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * kFwdWaves + wu) * 512);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i)
-      load_lds16(base + (ragged ? clamp_off(i, j0, ldv[i]) : ldv[i]),
-                 dV + (i * kFwdWaves + wu) * 512);
+      for (int i = 0; i < NLOAD; ++i)
+        load_lds16_off(base, clamp_off(i, j0, ld[i]), dst + (i * kFwdWaves + wu) * 512);
+    }
   };
+  auto issue_k = [&](int t, uint16_t* dK) { issue(Kb, ldk, t, dK); };
+  auto issue_v = [&](int t, uint16_t* dV) { issue(Vb, ldv, t, dV); };
   // K runs one tile ahead of V: tile t's scores are computed while tile t-1's
   // probabilities meet V.
   if (ntiles > 0) {
@@ -348,26 +354,39 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const float l = sum_halves(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   constexpr int OSW = CPR < 16 ? CPR - 1 : 15;
-  __syncthreads();  // all waves are done with the K/V tiles
-  uint16_t* so = (w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1;
+  if constexpr (kStageO) {
+    __syncthreads();  // all waves are done with the K/V tiles
+    uint16_t* so = (w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int d = 32 * db + 8 * a4 + 4 * hf;
-      u32x2 val = {Ops<T>::pack2(acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv),
-                   Ops<T>::pack2(acc[db][4 * a4 + 2] * inv, acc[db][4 * a4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(so + l32 * D + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * db + 8 * a4 + 4 * hf;
+        u32x2 val = {Ops<T>::pack2(acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv),
+                     Ops<T>::pack2(acc[db][4 * a4 + 2] * inv, acc[db][4 * a4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(so + l32 * D + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int p = lane + 64 * i;
+      const int row = p / CPR, c = p % CPR;
+      const int q = qw0 + row;
+      if (q < Lq)
+        store16(O + ((long)b * Lq + q) * qstride + (long)h * D + 8 * c,
+                *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))));
     }
-  __syncthreads();
+  } else if (qrow < Lq) {
+    uint16_t* Orow = O + ((long)b * Lq + qrow) * qstride + (long)h * D;
 #pragma unroll
-  for (int i = 0; i < 32 * CPR / 64; ++i) {
-    const int p = lane + 64 * i;
-    const int row = p / CPR, c = p % CPR;
-    const int q = qw0 + row;
-    if (q < Lq)
-      store16(O + ((long)b * Lq + q) * qstride + (long)h * D + 8 * c,
-              *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))));
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * db + 8 * a4 + 4 * hf;
+        u32x2 val = {Ops<T>::pack2(acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv),
+                     Ops<T>::pack2(acc[db][4 * a4 + 2] * inv, acc[db][4 * a4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(Orow + d) = val;
+      }
   }
   if (hf == 0 && qrow < Lq)
     LSE[(long)bh * Lq + qrow] = l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;

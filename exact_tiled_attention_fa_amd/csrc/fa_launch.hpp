@@ -39,7 +39,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 
 // Prefill tiling, reported by fa_info().
-constexpr int kFwdWaves = 4;           // wavefronts per workgroup
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 4
+#endif
+constexpr int kFwdWaves = FA_FWD_WAVES;  // wavefronts per workgroup
 constexpr int kFwdRowsPerWave = 32;    // query rows per wavefront
 constexpr int kFwdBM = kFwdWaves * kFwdRowsPerWave;
 constexpr int kDecodeKeysPerStep = 16;
