@@ -57,6 +57,14 @@ constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with it
 #ifndef FA_FWD_BN_D128
 #define FA_FWD_BN_D128 32
 #endif
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 2
+#endif
+// K/V tiles in flight: tile t+NS-1 (and K one further) is requested while
+// tile t is computed, which covers the HBM/L2 latency of the copies.
+constexpr int kStages = FA_FWD_STAGES;
+static_assert(kStages == 2 || kStages == 4, "stage count");
+
 template <int D> struct FwdTile { static constexpr int BN = FA_FWD_BN_D64; };
 template <> struct FwdTile<128> { static constexpr int BN = FA_FWD_BN_D128; };
 template <> struct FwdTile<256> { static constexpr int BN = 32; };
@@ -86,13 +94,28 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // The output is staged through LDS (one tile array per wave) when four
   // waves' 32 x D tiles fit; otherwise it is stored straight from registers.
   constexpr bool kStageO = kFwdWaves == 4 && 32 * D <= TILE;
-  // Two stages of K and V tiles.  Four distinct arrays (not slices of one)
+  // kStages stages of K and V tiles.  Distinct arrays (not slices of one)
   // let the compiler see that reading one stage does not alias the
-  // LDS-direct copy into the other, so it inserts no wait between them.
+  // LDS-direct copy into another, so it inserts no wait between them.
+  constexpr int T2 = kStages > 2 ? TILE : 16;
   __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK2[T2];
+  __shared__ __attribute__((aligned(16))) uint16_t sV2[T2];
+  __shared__ __attribute__((aligned(16))) uint16_t sK3[T2];
+  __shared__ __attribute__((aligned(16))) uint16_t sV3[T2];
+  auto kst = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return sK0; else if constexpr (i == 1) return sK1;
+    else if constexpr (i == 2) return sK2; else return sK3;
+  };
+  auto vst = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return sV0; else if constexpr (i == 1) return sV1;
+    else if constexpr (i == 2) return sV2; else return sV3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,14 +185,6 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   auto issue_k = [&](int t, uint16_t* dK) { issue(Kb, ldk, t, dK); };
   auto issue_v = [&](int t, uint16_t* dV) { issue(Vb, ldv, t, dV); };
-  // K runs one tile ahead of V: tile t's scores are computed while tile t-1's
-  // probabilities meet V.
-  if (ntiles > 0) {
-    issue_k(0, sK0);
-    issue_v(0, sV0);
-  }
-  if (ntiles > 1) issue_k(1, sK1);
-
   // Q^T operand: lane holds query `qrow`, 8 dims per 16-dim k-step.
   u32x4 qf[D / 16];
 #pragma unroll
@@ -294,29 +309,49 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
+  // Tile t's K and V live in stage t % kStages.  Requests run kStages-1
+  // tiles ahead (K one tile further, since S(t+1) is computed during step t)
+  // and are always issued -- past the last tile they re-read it -- so the
+  // number of copies in flight, and the wait below, is the same every step.
+  constexpr int kPerTile = 2 * NLOAD;  // copies per thread per step (K and V)
+  auto tile_wait_barrier = [&](auto young_tag) {
+    // This wave's copies older than the `young` most recent have landed and
+    // its LDS reads are done; then the workgroup barrier.  (No __syncthreads:
+    // its fence would also drain the copies still in flight.)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(young_tag)::value) & ~0x0F00);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  auto clampt = [&](int t) { return min(t, ntiles - 1); };
+
   // One pipeline step for tile t: its scores sc are folded already, K(t+1)
-  // sits in kn and V(t) in vc.  Refills the buffers of K(t) and V(t-1) with
-  // K(t+2) and V(t+1), then computes P(t), S(t+1) and P(t) V(t).  In the
-  // main phase (TAIL false) tiles t and t+1 are fully visible to every row of
-  // the workgroup, so nothing is masked or skipped.
-  auto step = [&](int t, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32], const uint16_t* kn,
-                  uint16_t* kfree, const uint16_t* vc, uint16_t* vn, auto tail_tag) {
+  // and V(t) have been requested kStages-1 steps ago.  Refills the stages of
+  // K(t) and V(t-1) with K(t+kStages) and V(t+kStages-1), then computes P(t),
+  // S(t+1) and P(t) V(t).  In the main phase (TAIL false) tiles t and t+1 are
+  // fully visible to every row of the workgroup, so nothing is masked or
+  // skipped.
+  auto step = [&](int t, auto I, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32], auto tail_tag) {
+    constexpr int i = decltype(I)::value;
     constexpr bool TAIL = decltype(tail_tag)::value;
-    wait_vmem();
-    __syncthreads();  // K(t+1), V(t) have landed; nobody reads K(t) or V(t-1) any more
-    if (t + 2 < ntiles) issue_k(t + 2, kfree);
-    if (t + 1 < ntiles) issue_v(t + 1, vn);
+    using Inext = std::integral_constant<int, (i + 1) % kStages>;
+    using Iprev = std::integral_constant<int, (i + kStages - 1) % kStages>;
+    tile_wait_barrier(std::integral_constant<int, (kStages - 2) * kPerTile>{});
+    issue_k(clampt(t + kStages), kst(I));
+    issue_v(clampt(t + kStages - 1), vst(Iprev{}));
     if (TAIL && t > last_live) return;  // every key of tile t is hidden from this wave
     uint32_t pk[BN / 32][8];
     make_p(sc, pk);
     if (!TAIL || t + 1 <= last_live) {
-      scores(sn, kn);
-      pv(pk, vc);
+      scores(sn, kst(Inext{}));
+      pv(pk, vst(I));
       fold(sn, t + 1, std::integral_constant<bool, TAIL>{});
     } else {
-      pv(pk, vc);
+      pv(pk, vst(I));
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2 % kStages>;
+  using S3 = std::integral_constant<int, 3 % kStages>;
 
   // Tiles [0, n_main) are seen whole by every row of the workgroup.
   const int kall = CAUSAL ? min(Lk, q0 + shift + 1) : Lk;
@@ -325,28 +360,50 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   using Tail = std::integral_constant<bool, true>;
 
   f32x16 sA[BN / 32], sB[BN / 32];
-  wait_vmem();
-  __syncthreads();  // K(0), V(0), K(1) have landed
-  if (0 <= last_live && ntiles > 0) {
-    scores(sA, sK0);
-    fold(sA, 0, Tail{});
+  if (ntiles > 0) {
+    // Prologue: K(0), then (K(j), V(j-1)) for j = 1 .. kStages-1.
+    issue_k(0, sK0);
+    issue_k(clampt(1), sK1);
+    issue_v(0, sV0);
+    if constexpr (kStages > 2) {
+      issue_k(clampt(2), kst(S2{}));
+      issue_v(clampt(1), sV1);
+      issue_k(clampt(3), kst(S3{}));
+      issue_v(clampt(2), vst(S2{}));
+    }
+    tile_wait_barrier(std::integral_constant<int, (kStages - 1) * kPerTile>{});  // K(0) landed
+    if (0 <= last_live) {
+      scores(sA, sK0);
+      fold(sA, 0, Tail{});
+    }
+    // Both phases walk kStages tiles at a time from t = 0, so stages and score
+    // arrays are in the same roles at every loop head.
+    int t = 0;
+    // Main phase: step t runs unmasked when tiles t and t+1 are both whole.
+    while (t + kStages < n_main) {
+      step(t, S0{}, sA, sB, Main{});
+      step(t + 1, S1{}, sB, sA, Main{});
+      if constexpr (kStages > 2) {
+        step(t + 2, S2{}, sA, sB, Main{});
+        step(t + 3, S3{}, sB, sA, Main{});
+      }
+      t += kStages;
+    }
+    // Tail phase: masked or partly skipped tiles (and the last whole ones).
+    while (t < ntiles) {
+      step(t, S0{}, sA, sB, Tail{});
+      if (t + 1 >= ntiles) break;
+      step(t + 1, S1{}, sB, sA, Tail{});
+      if constexpr (kStages > 2) {
+        if (t + 2 >= ntiles) break;
+        step(t + 2, S2{}, sA, sB, Tail{});
+        if (t + 3 >= ntiles) break;
+        step(t + 3, S3{}, sB, sA, Tail{});
+      }
+      t += kStages;
+    }
   }
-  // Both phases walk tiles in pairs from an even index, so the score arrays
-  // and stage buffers are in the same roles at every loop head.
-  int t = 0;
-  // Main phase: step t runs unmasked when tiles t and t+1 are both whole.
-  while (t + 2 < n_main) {
-    step(t, sA, sB, sK1, sK0, sV0, sV1, Main{});
-    step(t + 1, sB, sA, sK0, sK1, sV1, sV0, Main{});
-    t += 2;
-  }
-  // Tail phase: masked or partly skipped tiles (and the last whole ones).
-  while (t < ntiles) {
-    step(t, sA, sB, sK1, sK0, sV0, sV1, Tail{});
-    if (t + 1 >= ntiles) break;
-    step(t + 1, sB, sA, sK0, sK1, sV1, sV0, Tail{});
-    t += 2;
-  }
+  wait_vmem();  // copies of re-read tiles past the end are still landing
 
   // Epilogue: full row sum, O = acc / l staged through LDS (wave w uses one
   // stage array, rows [32][D] with 16-byte chunks XOR-swizzled by row), then
