@@ -11,6 +11,10 @@ Contents
 ``attention.attention_ref``
     The plain definition of softmax attention (scores, mask, row softmax,
     weighted sum of values, per-row logsumexp), evaluated in float64.
+``attention.varlen_ref``
+    Block-diagonal packing (several sequences in one row range, given by
+    cumulative offsets), each attending only to itself; also takes a
+    sliding window (left, right) like ``attention_ref``.
 ``attention.decode_ref``
     The same definition for one query token per sequence against a padded
     KV cache with per-sequence lengths.
@@ -25,13 +29,15 @@ than itself: a 40-digit ``decimal`` brute force, PyTorch's fp64 CPU
 ``scaled_dot_product_attention``, closed forms and invariants.
 """
 
-from .attention import attention_ref, decode_ref, causal_allowed
+from .attention import attention_ref, causal_allowed, decode_ref, key_bounds, varlen_ref
 from .online import online_attention_ref, split_combine_ref
 
 __all__ = [
     "attention_ref",
     "decode_ref",
     "causal_allowed",
+    "key_bounds",
+    "varlen_ref",
     "online_attention_ref",
     "split_combine_ref",
 ]

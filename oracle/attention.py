@@ -37,6 +37,13 @@ Sources (page title, section):
 * Causal alignment when Lq != Lk is not on the pages; read as bottom-right
   (the last query row sees every key), which equals the usual lower triangle
   when Lq == Lk and makes a one-token decode see its whole cache.
+* "5 years, 10K stars: xformers" (cloud.tencent.com) lists structured masks
+  that spare the kernel a dense mask read: causal, local (sliding window) and
+  block-diagonal (several sequences packed into one batch row).  Read here as
+  a window (left, right): row i sees keys j with i + shift - left <= j <=
+  i + shift + right, a negative bound meaning unbounded on that side (causal
+  additionally caps j <= i + shift); and block-diagonal packing as sequences
+  given by cumulative offsets cu_q / cu_k, each attending only to itself.
 
 Implementation notes: each (b, h) pair is independent; rows are processed in
 blocks of ``row_block`` so that at most row_block x Lk scores exist at once.
@@ -72,7 +79,28 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _head_attention(qh, kh, vh, scale, causal, row_block):
+def row_bounds(rows, Lq: int, Lk: int, causal: bool, window=(-1, -1)):
+    """Inclusive key ranges [lo, hi] that query rows ``rows`` may see
+    (lo > hi: none), as two integer arrays."""
+    left, right = window
+    rows = np.asarray(rows, dtype=np.int64)
+    shift = Lk - Lq
+    lo = np.zeros_like(rows) if left < 0 else np.maximum(0, rows + shift - left)
+    hi = np.full_like(rows, Lk - 1)
+    if right >= 0:
+        hi = np.minimum(hi, rows + shift + right)
+    if causal:
+        hi = np.minimum(hi, rows + shift)
+    return lo, hi
+
+
+def key_bounds(i: int, Lq: int, Lk: int, causal: bool, window=(-1, -1)):
+    """Inclusive range [lo, hi] of keys query row i may see (lo > hi: none)."""
+    lo, hi = row_bounds([i], Lq, Lk, causal, window)
+    return int(lo[0]), int(hi[0])
+
+
+def _head_attention(qh, kh, vh, scale, causal, row_block, window=(-1, -1)):
     """Plain attention for one (batch, head): qh [Lq,D], kh/vh [Lk,D]."""
     Lq, D = qh.shape
     Lk = kh.shape[0]
@@ -81,25 +109,22 @@ def _head_attention(qh, kh, vh, scale, causal, row_block):
     lse = np.full((Lq,), -np.inf, dtype=np.float64)
     if Lk == 0:
         return out, lse
-    shift = Lk - Lq
     for r0 in range(0, Lq, row_block):
         r1 = min(Lq, r0 + row_block)
-        kend = Lk
-        if causal:
-            kend = min(Lk, (r1 - 1) + shift + 1)
-            if kend <= 0:
-                continue  # every row of this block has an empty key set
-        s = scale * (qh[r0:r1] @ kh[:kend].T)  # [rows, kend]
-        if causal:
-            rows = np.arange(r0, r1)[:, None]
-            cols = np.arange(kend)[None, :]
-            s = np.where(cols <= rows + shift, s, -np.inf)
+        lo, hi = row_bounds(np.arange(r0, r1), Lq, Lk, causal, window)
+        kbeg = max(0, int(lo.min()))
+        kend = min(Lk, int(hi.max()) + 1)
+        if kend <= kbeg:
+            continue  # every row of this block has an empty key set
+        s = scale * (qh[r0:r1] @ kh[kbeg:kend].T)  # [rows, kend - kbeg]
+        cols = np.arange(kbeg, kend)[None, :]
+        s = np.where((cols >= lo[:, None]) & (cols <= hi[:, None]), s, -np.inf)
         m = s.max(axis=1)
         nonempty = np.isfinite(m)
         m_safe = np.where(nonempty, m, 0.0)
         p = np.exp(s - m_safe[:, None])  # exp(-inf) = 0 on masked keys
         l = p.sum(axis=1)
-        o = p @ vh[:kend]
+        o = p @ vh[kbeg:kend]
         with np.errstate(divide="ignore", invalid="ignore"):
             o = np.where(nonempty[:, None], o / l[:, None], 0.0)
             blk_lse = np.where(nonempty, m_safe + np.log(l), -np.inf)
@@ -116,14 +141,16 @@ def _default_workers() -> int:
 
 
 def attention_ref(q, k, v, scale: float, causal: bool, *, row_block: int = 1024,
-                  workers: int | None = None, heads=None):
+                  workers: int | None = None, heads=None, window=(-1, -1)):
     """Plain fp64 attention.
 
     q: [B, Lq, Hq, D]; k, v: [B, Lk, Hkv, D] (any float type; converted to
     float64 exactly).  ``scale`` is applied as given (pass the float32 value
     that the GPU receives).  Returns (O [B, Lq, Hq, D], lse [B, Hq, Lq]) in
     float64.  ``heads`` optionally restricts the work to a list of (b, h)
-    pairs; other outputs are left as NaN.
+    pairs; other outputs are left as NaN.  ``window`` = (left, right) limits
+    row i to keys i + Lk - Lq - left .. i + Lk - Lq + right (negative: no
+    limit on that side).
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -144,7 +171,7 @@ def attention_ref(q, k, v, scale: float, causal: bool, *, row_block: int = 1024,
         b, h = job
         kv = h // g
         o, l = _head_attention(q[b, :, h, :], k[b, :, kv, :], v[b, :, kv, :],
-                               scale, causal, row_block)
+                               scale, causal, row_block, tuple(window))
         out[b, :, h, :] = o
         lse[b, h, :] = l
 
@@ -191,4 +218,35 @@ def decode_ref(q, k_cache, v_cache, seqlens, scale: float, *, heads=None):
                                float(scale), False, 1)
         out[b, h, :] = o[0]
         lse[b, h] = l[0]
+    return out, lse
+
+
+def varlen_ref(q, k, v, cu_q, cu_k, scale: float, causal: bool, *, window=(-1, -1),
+               workers: int | None = None, heads=None):
+    """Block-diagonal packing: sequence b is rows cu_q[b] .. cu_q[b+1]-1 of
+    q [total_q, Hq, D] and rows cu_k[b] .. cu_k[b+1]-1 of k, v [total_k, Hkv, D];
+    each sequence attends only to its own keys, with the causal / window
+    rules of ``attention_ref`` applied inside it.  Returns (O [total_q, Hq, D],
+    lse [Hq, total_q]).  ``heads`` optionally restricts to (b, h) pairs.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    cu_q = [int(x) for x in np.asarray(cu_q).reshape(-1)]
+    cu_k = [int(x) for x in np.asarray(cu_k).reshape(-1)]
+    B = len(cu_q) - 1
+    total_q, Hq, _ = q.shape
+    out = np.full((total_q, Hq, v.shape[2]), np.nan)
+    lse = np.full((Hq, total_q), np.nan)
+    for b in range(B):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        hs = None if heads is None else [(0, h) for (bb, h) in heads if bb == b]
+        if hs is not None and not hs:
+            continue
+        if q1 <= q0:
+            continue
+        o_b, l_b = attention_ref(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], scale, causal,
+                                 window=window, workers=workers, heads=hs)
+        sel = range(Hq) if hs is None else [h for _, h in hs]
+        for h in sel:
+            out[q0:q1, h] = o_b[0, :, h]
+            lse[h, q0:q1] = l_b[0, h]
     return out, lse

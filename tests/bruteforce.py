@@ -12,8 +12,11 @@ from decimal import Decimal, localcontext
 import numpy as np
 
 
-def attention_decimal(q, k, v, scale, causal):
-    """q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] float arrays -> (O, lse) as float64."""
+def attention_decimal(q, k, v, scale, causal, window=(-1, -1)):
+    """q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] float arrays -> (O, lse) as float64.
+
+    ``window`` = (left, right): row i sees keys from i + Lk - Lq - left to
+    i + Lk - Lq + right (a negative value leaves that side open)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -29,7 +32,11 @@ def attention_decimal(q, k, v, scale, causal):
             for h in range(Hq):
                 kv = h // grp
                 for i in range(Lq):
-                    keys = [j for j in range(Lk) if (not causal) or j <= i + Lk - Lq]
+                    diag = i + Lk - Lq  # the key on this row's diagonal
+                    keys = [j for j in range(Lk)
+                            if ((not causal) or j <= diag)
+                            and (window[0] < 0 or j >= diag - window[0])
+                            and (window[1] < 0 or j <= diag + window[1])]
                     if not keys:
                         O[b, i, h, :] = 0.0
                         lse[b, h, i] = -np.inf

@@ -229,6 +229,53 @@ def pin_large_scores(attn):
     assert_close(l, np.array(1000 + math.log(z)).reshape(l.shape), 1e-12, "large scores lse")
 
 
+# (B, Lq, Lk, Hq, Hkv, D, causal, scale, window)
+WINDOW_CASES = [
+    (1, 6, 6, 1, 1, 2, False, 0.8, (1, 2)),
+    (1, 5, 7, 2, 1, 2, True, 0.6, (2, -1)),
+    (1, 6, 4, 1, 1, 3, False, 1.1, (0, 0)),
+    (1, 4, 6, 2, 2, 2, True, 0.5, (-1, 3)),
+]
+
+
+def pin_window_bruteforce(attn, tol=1e-13):
+    for n, (B, Lq, Lk, Hq, Hkv, D, causal, scale, win) in enumerate(WINDOW_CASES):
+        q, k, v = rand_qkv(150 + n, B, Lq, Lk, Hq, Hkv, D, scale_q=1.5)
+        o, l = attn(q, k, v, scale, causal, window=win)
+        ob, lb = attention_decimal(q, k, v, scale, causal, window=win)
+        assert_close(o, ob, tol, f"window brute O case {n}")
+        assert_close(l, lb, tol, f"window brute lse case {n}")
+
+
+def pin_window_closed_forms(attn):
+    """Window (0, 0) leaves each row its diagonal key; Q = 0 turns any window
+    into a plain mean over it; open windows reduce to the unwindowed cases."""
+    q, k, v = rand_qkv(160, 1, 9, 9, 2, 2, 4)
+    o, l = attn(q, k, v, 0.7, False, window=(0, 0))
+    assert_close(o, v, 1e-15, "window (0,0) O")
+    assert_close(l, 0.7 * np.einsum("blhd,blhd->bhl", q, k), 1e-14, "window (0,0) lse")
+    L, left, right = 13, 3, 2
+    _, k, v = rand_qkv(161, 1, L, L, 1, 1, 4)
+    q = np.zeros((1, L, 1, 4))
+    o, l = attn(q, k, v, 0.5, False, window=(left, right))
+    for i in range(L):
+        lo, hi = max(0, i - left), min(L - 1, i + right)
+        assert_close(o[0, i, 0], v[0, lo:hi + 1, 0].mean(0), 1e-14, f"window mean row {i}")
+        assert abs(l[0, 0, i] - math.log(hi - lo + 1)) <= 1e-14
+    q, k, v = rand_qkv(162, 1, 11, 11, 2, 1, 4)
+    for causal in (False, True):
+        o1, l1 = attn(q, k, v, 0.4, causal)
+        o2, l2 = attn(q, k, v, 0.4, causal, window=(-1, -1))
+        o3, l3 = attn(q, k, v, 0.4, causal, window=(11, 11))
+        assert_close(o2, o1, 0.0, "open window O")
+        assert_close(o3, o1, 1e-15, "wide window O")
+        assert_close(l3, l1, 1e-15, "wide window lse")
+    o1, l1 = attn(q, k, v, 0.4, True)
+    o2, l2 = attn(q, k, v, 0.4, False, window=(-1, 0))
+    assert_close(o2, o1, 1e-15, "window (-1,0) == causal O")
+    assert_close(l2, l1, 1e-15, "window (-1,0) == causal lse")
+
+
 ALL_PINS = [
     pin_bruteforce,
     pin_torch_sdpa,
@@ -243,4 +290,6 @@ ALL_PINS = [
     pin_bounds,
     pin_hand_cases,
     pin_large_scores,
+    pin_window_bruteforce,
+    pin_window_closed_forms,
 ]

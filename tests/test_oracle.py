@@ -3,6 +3,7 @@
 from __future__ import annotations
 
 import inspect
+import math
 import textwrap
 
 import numpy as np
@@ -68,6 +69,36 @@ def test_decode_never_reads_padding_and_handles_empty():
     assert np.all(o[1] == 0) and np.all(l[1] == -np.inf)
 
 
+def test_varlen_closed_form_and_no_leakage():
+    """Packed sequences attend only to themselves: with Q = 0 every row of
+    sequence b is the mean of b's own (visible) values, so any leakage of
+    keys across a sequence boundary changes the result."""
+    r = np.random.default_rng(17)
+    lens_q, lens_k = [3, 1, 5], [4, 2, 5]
+    cu_q, cu_k = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    v = r.standard_normal((cu_k[-1], 2, 4)) + 10 * np.arange(cu_k[-1])[:, None, None]
+    k = r.standard_normal((cu_k[-1], 2, 4))
+    q = np.zeros((cu_q[-1], 2, 4))
+    for causal in (False, True):
+        o, l = oracle.varlen_ref(q, k, v, cu_q, cu_k, 0.5, causal)
+        for b in range(3):
+            for i in range(lens_q[b]):
+                n = min(lens_k[b], i + lens_k[b] - lens_q[b] + 1) if causal else lens_k[b]
+                vis = v[cu_k[b]:cu_k[b] + n]
+                assert_close(o[cu_q[b] + i], vis.mean(0), 1e-13, f"varlen mean b={b} i={i}")
+                assert np.allclose(l[:, cu_q[b] + i], math.log(n), atol=1e-14)
+
+
+def test_varlen_equal_lengths_is_the_dense_batch():
+    q, k, v = rand_qkv(18, 3, 7, 9, 4, 2, 8)
+    for causal, win in ((False, (-1, -1)), (True, (-1, -1)), (False, (2, 1)), (True, (3, -1))):
+        o1, l1 = oracle.attention_ref(q, k, v, 0.3, causal, window=win)
+        o2, l2 = oracle.varlen_ref(q.reshape(21, 4, 8), k.reshape(27, 2, 8), v.reshape(27, 2, 8),
+                                   [0, 7, 14, 21], [0, 9, 18, 27], 0.3, causal, window=win)
+        assert_close(o2, o1.reshape(21, 4, 8), 1e-15, "varlen vs dense O")
+        assert_close(l2, l1.transpose(1, 0, 2).reshape(4, 21), 1e-15, "varlen vs dense lse")
+
+
 def test_row_blocking_is_invisible():
     q, k, v = rand_qkv(15, 1, 50, 50, 2, 2, 8)
     for causal in (False, True):
@@ -82,18 +113,25 @@ def test_row_blocking_is_invisible():
 # into its source; at least one pin must reject it.
 # ---------------------------------------------------------------------------
 HEAD_MUTATIONS = {
-    "mask_off_by_one": ("cols <= rows + shift", "cols < rows + shift"),
-    "mask_top_left": ("cols <= rows + shift", "cols <= rows"),
-    "dropped_scale": ("s = scale * (qh[r0:r1] @ kh[:kend].T)", "s = (qh[r0:r1] @ kh[:kend].T)"),
-    "sign_flip": ("s = scale * (qh[r0:r1] @ kh[:kend].T)", "s = -scale * (qh[r0:r1] @ kh[:kend].T)"),
-    "value_rows_reversed": ("o = p @ vh[:kend]", "o = p @ vh[:kend][::-1]"),
+    "dropped_scale": ("s = scale * (qh[r0:r1] @ kh[kbeg:kend].T)", "s = (qh[r0:r1] @ kh[kbeg:kend].T)"),
+    "sign_flip": ("s = scale * (qh[r0:r1] @ kh[kbeg:kend].T)",
+                  "s = -scale * (qh[r0:r1] @ kh[kbeg:kend].T)"),
+    "value_rows_reversed": ("o = p @ vh[kbeg:kend]", "o = p @ vh[kbeg:kend][::-1]"),
     "lse_drops_max": ("m_safe + np.log(l)", "np.log(l)"),
     "no_max_subtraction": ("p = np.exp(s - m_safe[:, None])", "p = np.exp(s)"),
     "no_normalisation": ("o / l[:, None]", "o"),
-    "drops_last_key": ("kend = min(Lk, (r1 - 1) + shift + 1)", "kend = min(Lk, (r1 - 1) + shift)"),
-    "transposed_operand": ("s = scale * (qh[r0:r1] @ kh[:kend].T)",
-                           "s = scale * (qh[r0:r1] @ kh[:kend].T).T[:r1 - r0, :kend] "
-                           "if kend == r1 - r0 else scale * (qh[r0:r1] @ kh[:kend].T)"),
+    "drops_last_key": ("kend = min(Lk, int(hi.max()) + 1)", "kend = min(Lk, int(hi.max()))"),
+    "mask_drops_low_bound": ("(cols >= lo[:, None]) & ", ""),
+    "transposed_operand": ("s = scale * (qh[r0:r1] @ kh[kbeg:kend].T)",
+                           "s = scale * (qh[r0:r1] @ kh[kbeg:kend].T).T[:r1 - r0, :kend - kbeg] "
+                           "if kend - kbeg == r1 - r0 else scale * (qh[r0:r1] @ kh[kbeg:kend].T)"),
+}
+BOUND_MUTATIONS = {
+    "mask_off_by_one": ("hi = np.minimum(hi, rows + shift)", "hi = np.minimum(hi, rows + shift - 1)"),
+    "mask_top_left": ("shift = Lk - Lq", "shift = 0"),
+    "window_left_off_by_one": ("np.maximum(0, rows + shift - left)",
+                               "np.maximum(0, rows + shift - left + 1)"),
+    "window_right_ignored": ("hi = np.minimum(hi, rows + shift + right)", "hi = hi"),
 }
 REF_MUTATIONS = {
     "gqa_modulo_mapping": ("kv = h // g", "kv = h % Hkv"),
@@ -127,6 +165,14 @@ def test_planted_mistake_in_head_is_caught(name, monkeypatch):
     old, new = HEAD_MUTATIONS[name]
     mutated, _ = _mutant(oatt._head_attention, old, new)
     monkeypatch.setattr(oatt, "_head_attention", mutated)
+    assert _rejected(oracle.attention_ref), f"no pin rejects mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(BOUND_MUTATIONS))
+def test_planted_mistake_in_mask_bounds_is_caught(name, monkeypatch):
+    old, new = BOUND_MUTATIONS[name]
+    mutated, _ = _mutant(oatt.row_bounds, old, new)
+    monkeypatch.setattr(oatt, "row_bounds", mutated)
     assert _rejected(oracle.attention_ref), f"no pin rejects mutant {name}"
 
 
