@@ -13,8 +13,14 @@ on the stream the kernel runs on; the decode half is reported in the same
 line as algorithmic HBM GB/s (K/V rows of each cache read once, q read, o and
 lse written).  ``ms_per_step`` is wall time per step over the K timed steps.
 
+The structured-mask prefill workloads (sliding window ``swa16k``, packed
+sequences ``varlen16``) are timed after the step loop, with HIP events around
+each launch, and reported under ``masks`` in the same line; they are not part
+of ``value``.
+
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--with-copy MIB] [--only prefill|decode] [--all-configs]
+                    [--with-copy MIB] [--only prefill|decode] [--no-masks]
+                    [--all-configs]
 """
 
 from __future__ import annotations
@@ -48,6 +54,8 @@ def parse():
     p.add_argument("--with-copy", type=int, default=0, metavar="MIB",
                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--no-masks", action="store_true",
+                   help="skip the structured-mask prefill workloads (sliding window, packed)")
     p.add_argument("--all-configs", action="store_true",
                    help="also print one extra JSON line per prefill workload")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -165,6 +173,52 @@ def cpu_baseline_decode(cfg, q, kc, vc, lens, scale, nseq=16):
             "sample": f"first {nseq} of {cfg.B} sequences, all heads, fp64 numpy, {dt:.2f} s wall"}
 
 
+def time_masked(cfg, dev, reps=10, warmup=3):
+    """Mean launch time (ms, HIP events on the launch stream) of one
+    structured-mask workload, and its algorithmic TFLOP/s."""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd, flash_attn_varlen
+
+    q, k, v, cu = (None if t is None else t.to(dev) for t in W.masked_inputs(cfg))
+    sc = float(np.float32(cfg.scale))
+    lmax = max(cfg.lengths())
+    o = torch.empty_like(q)
+    if cfg.packed:
+        lse = torch.empty((cfg.Hq, q.shape[0]), dtype=torch.float32, device=dev)
+        run = lambda: flash_attn_varlen(q, k, v, cu, cu, lmax, lmax, softmax_scale=sc,
+                                        causal=cfg.causal, window=cfg.window, out=o, lse=lse)
+    else:
+        lse = torch.empty((cfg.nseq, cfg.Hq, lmax), dtype=torch.float32, device=dev)
+        run = lambda: flash_attn_fwd(q, k, v, softmax_scale=sc, causal=cfg.causal,
+                                     window=cfg.window, out=o, lse=lse)
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    mean = float(np.mean(ms))
+    tf = cfg.flops() / (mean * 1e-3) / 1e12
+    lens = cfg.lengths()
+    return {"workload": f"{cfg.nseq} x L={'%d' % lens[0] if cfg.len_lo == cfg.len_hi else 'U[%d,%d]' % (cfg.len_lo, cfg.len_hi)}"
+                        f" Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} {str(cfg.dtype)[6:]}"
+                        f" causal={cfg.causal} window={tuple(cfg.window)}"
+                        f" {'packed' if cfg.packed else 'dense'}",
+            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
+                   "min": round(float(np.min(ms)), 5)},
+            "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}}
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -268,7 +322,7 @@ def main():
                            "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
                            "traffic": traffic_for("fwd_kernel", source_digest(
                                ["fa_fwd.hip", "fa_common.hpp"])),
-                           "kernel": "fwd_kernel<bf16_t,128,64,true>",
+                           "kernel": "fwd_kernel<bf16_t, 128, true>",
                            "alg_flops_per_launch": pcfg.flops()}
     if do_dec:
         dms = float(np.mean(dec_ms))
@@ -285,6 +339,9 @@ def main():
                                           ["fa_decode.hip", "fa_common.hpp"]))}}
         if out["value"] is None:
             out["value"], out["unit"] = round(gbs, 2), "GB/s"
+    if do_pf and not args.no_masks:
+        print("# structured-mask workloads", file=sys.stderr, flush=True)
+        out["masks"] = {name: time_masked(cfg, dev) for name, cfg in W.MASKED.items()}
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         if do_pf:

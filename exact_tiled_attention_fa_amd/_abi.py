@@ -33,6 +33,8 @@ _F = ctypes.c_float
 _Z = ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                       _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
     "fa_last_error": (ctypes.c_char_p, []),
@@ -71,6 +73,13 @@ def load() -> ctypes.CDLL:
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype, stream) -> int:
     """Raw C call; pointers are ints (device addresses), returns the status."""
     return load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, dtype, stream)
+
+
+def fa_fwd_ex(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Lq, Lk, total_q, total_k,
+              D, scale, causal, window_left, window_right, dtype, stream) -> int:
+    return load().fa_fwd_ex(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Lq, Lk,
+                            total_q, total_k, D, scale, causal, window_left, window_right, dtype,
+                            stream)
 
 
 def fa_decode_workspace_size(B, Hq, D, num_splits) -> int:

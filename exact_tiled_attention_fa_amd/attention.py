@@ -41,11 +41,14 @@ def _stream_handle(device: torch.device) -> int:
 
 
 def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, softmax_scale=None,
-                   causal: bool = False, dropout_p: float = 0.0, out=None, lse=None):
+                   causal: bool = False, dropout_p: float = 0.0, window=(-1, -1), out=None,
+                   lse=None):
     """Exact attention forward.  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] (fp16/bf16).
 
     Returns (o [B,Lq,Hq,D] in q's dtype, lse [B,Hq,Lq] float32).  Causal
     masking is bottom-right aligned (row i sees keys j <= i + Lk - Lq).
+    ``window`` = (left, right) limits row i to keys i+Lk-Lq-left ..
+    i+Lk-Lq+right (a negative value leaves that side open).
     """
     if dropout_p != 0.0:
         raise ValueError("dropout_p must be 0.0 (the forward has no dropout)")
@@ -64,11 +67,57 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, softmax
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
-    st = _abi.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     B, Hq, Hkv, Lq, Lk, D, scale, 1 if causal else 0, _DTYPES[q.dtype],
-                     _stream_handle(q.device))
+    wl, wr = (int(window[0]), int(window[1]))
+    if wl < 0 and wr < 0:
+        st = _abi.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, Hq, Hkv, Lq, Lk, D, scale, 1 if causal else 0, _DTYPES[q.dtype],
+                         _stream_handle(q.device))
+        where = "fa_fwd"
+    else:
+        st = _abi.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), None, None, B, Hq, Hkv, Lq, Lk, 0, 0, D, scale,
+                            1 if causal else 0, wl, wr, _DTYPES[q.dtype], _stream_handle(q.device))
+        where = "fa_fwd_ex"
     if st != _abi.FA_OK:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, where)
+    return out, lse
+
+
+def flash_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                      cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
+                      softmax_scale=None, causal: bool = False, window=(-1, -1), out=None,
+                      lse=None):
+    """Packed sequences: q [total_q,Hq,D], k/v [total_k,Hkv,D]; cu_seqlens_*
+    int32 [B+1] cumulative offsets on the device; each sequence attends only
+    to itself.  Returns (o [total_q,Hq,D], lse [Hq,total_q] float32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens_q, "cu_seqlens_q"),
+                 (cu_seqlens_k, "cu_seqlens_k")):
+        _check_dev(t, n)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("expected q [total_q,Hq,D] and k, v [total_k,Hkv,D]")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if Dk != D:
+        raise ValueError("head_dim mismatch between q and k")
+    B = cu_seqlens_q.shape[0] - 1
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = _abi.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv,
+                        int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, D, scale,
+                        1 if causal else 0, int(window[0]), int(window[1]), _DTYPES[q.dtype],
+                        _stream_handle(q.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_fwd_ex")
     return out, lse
 
 

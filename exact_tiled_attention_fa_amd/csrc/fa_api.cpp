@@ -51,11 +51,28 @@ extern "C" {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                  int Hkv, int Lq, int Lk, int D, float scale, int causal, fa_dtype dtype,
                  hipStream_t stream) {
+  return fa_fwd_ex(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, 0, 0, D, scale, causal,
+                   -1, -1, dtype, stream);
+}
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int Lq, int Lk, int total_q, int total_k, int D, float scale, int causal,
+                    int window_left, int window_right, fa_dtype dtype, hipStream_t stream) {
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(k, "k"));
   FA_TRY(check_ptr(v, "v"));
   FA_TRY(check_ptr(o, "o"));
   FA_TRY(check_ptr(lse, "lse"));
+  const bool packed = cu_seqlens_q != nullptr || cu_seqlens_k != nullptr;
+  if (packed) {
+    if (!cu_seqlens_q || !cu_seqlens_k)
+      return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");
+    if (((uintptr_t)cu_seqlens_q & 3u) || ((uintptr_t)cu_seqlens_k & 3u))
+      return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens arrays are not 4-byte aligned");
+    if (total_q < 1 || total_k < 1)
+      return fail(FA_ERR_INVALID_ARGUMENT, "total_q=%d and total_k=%d must be >= 1", total_q, total_k);
+  }
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || D < 1)
     return fail(FA_ERR_INVALID_ARGUMENT,
                 "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d)", B, Hq, Hkv, Lq, Lk, D);
@@ -66,16 +83,35 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)dtype);
   if (!head_dim_supported(D))
     return fail(FA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", D);
+  // The kernel addresses a K/V tile with 32-bit byte offsets: 64 rows of
+  // Hkv * D elements must stay below 4 GiB.
+  if ((long long)Hkv * D >= (1LL << 25))
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hkv * D = %lld must be < 2^25", (long long)Hkv * D);
   const long long nqt = ((long long)Lq + fa::kFwdBM - 1) / fa::kFwdBM;
   if (nqt * B * Hq > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (Lq/%d * B * Hq > 2^31-1)", fa::kFwdBM);
-  if ((long long)B * Lq * Hq > 0x7fffffffLL || (long long)B * Lk * Hkv > 0x7fffffffLL)
-    return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
+  const long long rows_q = packed ? (long long)total_q : (long long)B * Lq;
+  const long long rows_k = packed ? (long long)total_k : (long long)B * Lk;
+  if (rows_q * Hq > 0x7fffffffLL || rows_k * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H (rows * heads) exceeds 2^31-1");
+  // Window bounds are evaluated in 32-bit arithmetic: a side at least as wide
+  // as every sequence is the same as no bound, and with a window the query
+  // plus key rows are kept below 2^30 so that i + (Lk - Lq) -/+ window fits.
+  const long long span = rows_q + rows_k;
+  const bool windowed = window_left >= 0 || window_right >= 0;
+  if (windowed && span > (1LL << 30))
+    return fail(FA_ERR_INVALID_ARGUMENT, "windowed attention needs query + key rows <= 2^30");
 
   fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal ? 1 : 0,
                 dtype == FA_BF16 ? 1 : 0};
+  a.win_left = (window_left < 0 || window_left >= span) ? -1 : window_left;
+  a.win_right = (window_right < 0 || window_right >= span) ? -1 : window_right;
+  a.cu_q = packed ? cu_seqlens_q : nullptr;
+  a.cu_k = packed ? cu_seqlens_k : nullptr;
+  a.total_q = packed ? total_q : 0;
+  a.total_k = packed ? total_k : 0;
   hipError_t e = fa::launch_fwd(a, stream);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "attention forward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -129,10 +165,11 @@ const char* fa_last_error(void) { return g_err; }
 
 const char* fa_info(void) {
   return "arch=gfx950; head_dims={64,128,256}; dtypes={f16,bf16}; "
-         "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), BN=64 keys, "
-         "mfma_f32_32x32x16, K/V^T tiles in LDS, causal tile skip, GQA; "
-         "decode: split-KV, 1 wave64 per (chunk, kv head, 16 heads, sequence), "
-         "mfma_f32_16x16x32, logsumexp combine; version=0.1.0";
+         "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), 32-key tiles (64 at D=64), "
+         "mfma_f32_32x32x16, LDS-direct K/V with transpose reads, causal/window tile "
+         "skip, block-diagonal packing, GQA; "
+         "decode: split-KV, 4 wave64 per (chunk, kv head, 16 heads, sequence), 16-key steps, "
+         "mfma_f32_16x16x32 + 16x16x16, logsumexp combine; version=0.2.0";
 }
 
 }  // extern "C"

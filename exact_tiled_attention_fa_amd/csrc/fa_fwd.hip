@@ -27,9 +27,15 @@
 //     V tile with ds_read_b64_tr_b16, which hands each lane one head-dim
 //     column of four consecutive keys.  The output accumulator keeps the
 //     query in the lane, so its rescale is lane-local.
-//   * Causal: KV tiles entirely above the diagonal are never loaded; only
-//     tiles that straddle the diagonal or the ragged key tail take the masked
-//     path.  Workgroups are issued heaviest query tile first.
+//   * Masks: each row sees keys [kmin, kmax] -- causal (bottom-right), a
+//     sliding window (left, right), the key count; xformers' structured masks
+//     ("5 years, 10K stars: xformers", cloud.tencent.com) are read this way.
+//     KV tiles no row of the workgroup sees are never loaded; tiles every row
+//     sees whole run a mask-free main loop, the few others a masked one.
+//     Workgroups are issued heaviest query tile first.
+//   * Block-diagonal packing: with cumulative offsets cu_q / cu_k, sequence b
+//     is rows cu_q[b] .. cu_q[b+1]-1 of Q/O (cu_k for K/V) and attends only to
+//     itself; without them the batch is dense [B, L, H, D].
 //   * Lazy rescaling: a row's reference max moves only when a new score
 //     exceeds it by more than 2^8 in the exponent, so the accumulator rescale
 //     (D/2 multiplies per lane) is rare; probabilities stay <= 256, inside
@@ -79,12 +85,28 @@ template <int D> __device__ __forceinline__ int swz_v(int r) {
   return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
+struct FwdParams {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  float* LSE;
+  const int* cu_q;  // nullptr: dense batch
+  const int* cu_k;
+  int B, Hq, Hkv;
+  int Lq, Lk;       // dense: sequence lengths; packed: the longest ones
+  int total_q, total_k;
+  int win_left, win_right;  // < 0: unbounded
+  float scale2, thr;
+  uint32_t qxor;
+};
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kNT, (D <= 128 ? 2 : 1))
-void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int B, int Hq, int Hkv, int Lq, int Lk,
-                float scale2, float thr, uint32_t qxor) {
+void fwd_kernel(const FwdParams prm) {
+  const int B = prm.B, Hq = prm.Hq, Hkv = prm.Hkv;
+  const float scale2 = prm.scale2, thr = prm.thr;
+  const uint32_t qxor = prm.qxor;
   constexpr int BM = kFwdBM;
   constexpr int BN = FwdTile<D>::BN;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -123,35 +145,77 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  // Block -> work item.  The work list is ordered (batch, query head, query
-  // tile heaviest first); query heads that share a K/V head are adjacent.
-  // Blocks are dealt to the XCDs round-robin (block i runs on XCD i % 8), so
-  // XCD x is given the x-th contiguous slice of the list: at any moment each
-  // XCD works on a few heads, whose K/V tiles then stay in its own L2.
-  const int nqt = (Lq + BM - 1) / BM;
-  const int N = nqt * B * Hq;
+  // Block -> work item.  Blocks are dealt to the XCDs round-robin (block i
+  // runs on XCD i % 8), and each XCD should get an equal share of the work
+  // with its K/V tiles staying in its own L2.  When Hq is a multiple of 8,
+  // XCD x takes query heads [x*Hq/8, (x+1)*Hq/8) of every sequence (the heads
+  // that share a K/V head are adjacent, so they land together), which keeps
+  // the XCDs balanced even when packed sequences differ in length.
+  // Otherwise XCD x takes the x-th contiguous slice of the (batch, head,
+  // query tile) list.  Either way an XCD walks its items sequence by sequence,
+  // head by head, heaviest query tile first.
+  const int nqt = (prm.Lq + BM - 1) / BM;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int item = xcd * (N / kXcds) + min(xcd, N % kXcds) + slot;
-  const int bh = item / nqt;
-  int qt = item - bh * nqt;
+  int b, h, qt;
+  if (Hq % kXcds == 0) {
+    const int hx = Hq / kXcds;
+    const int per_b = hx * nqt;
+    b = slot / per_b;
+    const int r = slot - b * per_b;
+    const int hh = r / nqt;
+    qt = r - hh * nqt;
+    h = xcd * hx + hh;
+  } else {
+    const int N = nqt * B * Hq;
+    const int item = xcd * (N / kXcds) + min(xcd, N % kXcds) + slot;
+    const int bhi = item / nqt;
+    qt = item - bhi * nqt;
+    b = bhi / Hq;
+    h = bhi - b * Hq;
+  }
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
+  const int bh = b * Hq + h;
   const int kvh = h / (Hq / Hkv);
-  const int shift = Lk - Lq;
+
+  // This sequence's rows.  Packed offsets are clamped into the tensors so
+  // that inconsistent offsets cannot move an access out of bounds.
+  int qs, Lq, ks, Lk;
+  if (prm.cu_q) {
+    qs = min(max(prm.cu_q[b], 0), prm.total_q);
+    Lq = min(max(prm.cu_q[b + 1], qs), prm.total_q) - qs;
+    ks = min(max(prm.cu_k[b], 0), prm.total_k);
+    Lk = min(max(prm.cu_k[b + 1], ks), prm.total_k) - ks;
+  } else {
+    qs = b * prm.Lq, Lq = prm.Lq, ks = b * prm.Lk, Lk = prm.Lk;
+  }
   const int q0 = qt * BM;
+  if (q0 >= Lq) return;  // past this sequence's rows (whole workgroup)
+  const int shift = Lk - Lq;
   const int qw0 = q0 + kFwdRowsPerWave * w;
   const int qrow = qw0 + l32;
 
+  // Keys row i may see: [kmin(i), kmax(i)], both non-decreasing in i.
+  const int wl = prm.win_left, wr = prm.win_right;
+  auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
+  auto kmax = [&](int i) {
+    int hi = Lk - 1;
+    if (CAUSAL) hi = min(hi, i + shift);
+    if (wr >= 0) hi = min(hi, i + shift + wr);
+    return hi;
+  };
+
   const long qstride = (long)Hq * D;
   const long kstride = (long)Hkv * D;
-  const uint16_t* Qb = Q + (long)b * Lq * qstride + (long)h * D;
-  const uint16_t* Kb = K + (long)b * Lk * kstride + (long)kvh * D;
-  const uint16_t* Vb = V + (long)b * Lk * kstride + (long)kvh * D;
+  const uint16_t* Qb = prm.Q + (long)qs * qstride + (long)h * D;
+  const uint16_t* Kb = prm.K + (long)ks * kstride + (long)kvh * D;
+  const uint16_t* Vb = prm.V + (long)ks * kstride + (long)kvh * D;
 
-  int kend = Lk;
-  if (CAUSAL) kend = min(Lk, min(q0 + BM, Lq) + shift);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // Tiles t_first .. t_first+ntiles-1 hold every key some row of the
+  // workgroup sees; below, u = t - t_first indexes them.
+  const int q_last = min(q0 + BM, Lq) - 1;
+  const int wg_lo = kmin(q0), wg_hi = kmax(q_last);
+  const int t_first = wg_lo / BN;
+  const int ntiles = wg_hi >= wg_lo ? wg_hi / BN - t_first + 1 : 0;
 
   // Loader: load i of this thread fills 16-byte chunk position P of the tile
   // (row P / CPR, stored chunk P % CPR holding logical chunk (P % CPR) ^ swz).
@@ -183,8 +247,8 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         load_lds16_off(base, clamp_off(i, j0, ld[i]), dst + (i * kFwdWaves + wu) * 512);
     }
   };
-  auto issue_k = [&](int t, uint16_t* dK) { issue(Kb, ldk, t, dK); };
-  auto issue_v = [&](int t, uint16_t* dV) { issue(Vb, ldv, t, dV); };
+  auto issue_k = [&](int u, uint16_t* dK) { issue(Kb, ldk, t_first + u, dK); };
+  auto issue_v = [&](int u, uint16_t* dV) { issue(Vb, ldv, t_first + u, dV); };
   // Q^T operand: lane holds query `qrow`, 8 dims per 16-dim k-step.
   u32x4 qf[D / 16];
 #pragma unroll
@@ -200,7 +264,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Per-lane LDS element offsets of the MFMA operand reads.
   int koff[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * D + 8 * ((2 * ks + hf) ^ swz_k<D>(l32));
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = l32 * D + 8 * ((2 * kk + hf) ^ swz_k<D>(l32));
   // V^T read for k-step t, half r, head-dim block db: row 16t + 8r + 4hf + (lane%16)/4,
   // columns 32db + 16*((lane/16)%2) + 4*(lane%4) .. +3.  swz_v depends only on the lane here.
   const int vrow = 4 * hf + ((lane & 15) >> 2);
@@ -211,10 +275,12 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     voff[db] = vrow * D + 8 * ((col >> 3) ^ swz_v<D>(vrow)) + (col & 7);
   }
 
-  const bool wave_live = qw0 < Lq;
   const int qw_last = min(qw0 + kFwdRowsPerWave - 1, Lq - 1);
-  const int wave_kmax = CAUSAL ? min(Lk - 1, qw_last + shift) : Lk - 1;
-  const int row_kmax = CAUSAL ? min(Lk - 1, qrow + shift) : Lk - 1;
+  const int row_kmin = kmin(qrow), row_kmax = kmax(qrow);
+  // Relative tiles first_live .. last_live hold keys some row of this wave sees.
+  const bool wave_live = qw0 < Lq && kmax(qw_last) >= kmin(qw0);
+  const int first_live = wave_live ? kmin(qw0) / BN - t_first : ntiles;
+  const int last_live = wave_live ? kmax(qw_last) / BN - t_first : -1;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -222,8 +288,6 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m_ref = -INFINITY;  // reference max (raw score units) of this lane's row
   float l_part = 0.f;       // this lane's half of the row sum (relative to m_ref)
 
-  // Tiles with index <= last_live hold at least one key some row of this wave sees.
-  const int last_live = wave_live && wave_kmax >= 0 ? wave_kmax / BN : -1;
 
   // S^T = K Q^T for BN keys x 32 queries (raw scores).
   auto scores = [&](f32x16 (&s)[BN / 32], const uint16_t* sK) {
@@ -231,9 +295,9 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int kb = 0; kb < BN / 32; ++kb) {
       s[kb] = (f32x16){};
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + 32 * kb * D + koff[ks]);
-        s[kb] = Ops<T>::mfma32(a, qf[ks], s[kb]);
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + 32 * kb * D + koff[kk]);
+        s[kb] = Ops<T>::mfma32(a, qf[kk], s[kb]);
       }
     }
   };
@@ -241,18 +305,19 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Folds tile t's row max into the reference max and rescales the
   // accumulator if it moved.  With MASK, first sets the scores of keys the row
   // may not see to -inf (only tiles crossing the diagonal or the key tail).
-  auto fold = [&](f32x16 (&s)[BN / 32], int t, auto mask_tag) {
+  auto fold = [&](f32x16 (&s)[BN / 32], int u, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int j0 = t * BN;
+    const int j0 = (t_first + u) * BN;
     float mx = -INFINITY;
-    if (MASK && ((j0 + BN > Lk) || (CAUSAL && j0 + BN - 1 > qw0 + shift))) {
-      // key j0 + 32kb + 8(r/4) + 4hf + r%4 is visible iff it is <= row_kmax
-      const int lim = row_kmax - j0 - 4 * hf;
+    if (MASK && (j0 < kmin(qw_last) || j0 + BN - 1 > kmax(qw0))) {
+      // key j0 + 32kb + 8(r/4) + 4hf + r%4 is visible iff it is in [row_kmin, row_kmax]
+      const int hi = row_kmax - j0 - 4 * hf, lo = row_kmin - j0 - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off > hi || off < lo) s[kb][r] = -INFINITY;
           mx = fmaxf(mx, s[kb][r]);
         }
     } else {
@@ -337,7 +402,12 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     tile_wait_barrier(std::integral_constant<int, (kStages - 2) * kPerTile>{});
     issue_k(clampt(t + kStages), kst(I));
     issue_v(clampt(t + kStages - 1), vst(Iprev{}));
-    if (TAIL && t > last_live) return;  // every key of tile t is hidden from this wave
+    if (TAIL && (t > last_live || t + 1 < first_live)) return;  // tile t and t+1 hidden from this wave
+    if (TAIL && t + 1 == first_live) {  // tile t hidden, t+1 the wave's first
+      scores(sn, kst(Inext{}));
+      fold(sn, t + 1, std::integral_constant<bool, true>{});
+      return;
+    }
     uint32_t pk[BN / 32][8];
     make_p(sc, pk);
     if (!TAIL || t + 1 <= last_live) {
@@ -353,9 +423,9 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   using S2 = std::integral_constant<int, 2 % kStages>;
   using S3 = std::integral_constant<int, 3 % kStages>;
 
-  // Tiles [0, n_main) are seen whole by every row of the workgroup.
-  const int kall = CAUSAL ? min(Lk, q0 + shift + 1) : Lk;
-  const int n_main = kall > 0 ? min(ntiles, kall / BN) : 0;
+  // Relative tiles [m_lo, m_hi) are seen whole by every row of the workgroup.
+  const int m_lo = max(0, (kmin(q_last) + BN - 1) / BN - t_first);
+  const int m_hi = min(ntiles, (kmax(q0) + 1) / BN - t_first);
   using Main = std::integral_constant<bool, false>;
   using Tail = std::integral_constant<bool, true>;
 
@@ -372,15 +442,30 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       issue_v(clampt(2), vst(S2{}));
     }
     tile_wait_barrier(std::integral_constant<int, (kStages - 1) * kPerTile>{});  // K(0) landed
-    if (0 <= last_live) {
+    if (first_live == 0 && last_live >= 0) {
       scores(sA, sK0);
       fold(sA, 0, Tail{});
     }
-    // Both phases walk kStages tiles at a time from t = 0, so stages and score
-    // arrays are in the same roles at every loop head.
+    // Every phase walks kStages tiles at a time from t = 0, so stages and
+    // score arrays are in the same roles at every loop head.
     int t = 0;
+    // Head phase (windows): masked tiles before the whole ones.  Running out
+    // of tiles here ends the walk (t = ntiles skips the later phases).
+    const int m_lo_al = (m_lo + kStages - 1) / kStages * kStages;
+    while (t < m_lo_al && t < ntiles) {
+      step(t, S0{}, sA, sB, Tail{});
+      if (t + 1 >= ntiles) { t = ntiles; break; }
+      step(t + 1, S1{}, sB, sA, Tail{});
+      if constexpr (kStages > 2) {
+        if (t + 2 >= ntiles) { t = ntiles; break; }
+        step(t + 2, S2{}, sA, sB, Tail{});
+        if (t + 3 >= ntiles) { t = ntiles; break; }
+        step(t + 3, S3{}, sB, sA, Tail{});
+      }
+      t += kStages;
+    }
     // Main phase: step t runs unmasked when tiles t and t+1 are both whole.
-    while (t + kStages < n_main) {
+    while (t >= m_lo && t + kStages < m_hi) {
       step(t, S0{}, sA, sB, Main{});
       step(t + 1, S1{}, sB, sA, Main{});
       if constexpr (kStages > 2) {
@@ -430,11 +515,11 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const int row = p / CPR, c = p % CPR;
       const int q = qw0 + row;
       if (q < Lq)
-        store16(O + ((long)b * Lq + q) * qstride + (long)h * D + 8 * c,
+        store16(prm.O + ((long)qs + q) * qstride + (long)h * D + 8 * c,
                 *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))));
     }
   } else if (qrow < Lq) {
-    uint16_t* Orow = O + ((long)b * Lq + qrow) * qstride + (long)h * D;
+    uint16_t* Orow = prm.O + ((long)qs + qrow) * qstride + (long)h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -445,8 +530,11 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         *reinterpret_cast<u32x2*>(Orow + d) = val;
       }
   }
-  if (hf == 0 && qrow < Lq)
-    LSE[(long)bh * Lq + qrow] = l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
+  if (hf == 0 && qrow < Lq) {
+    // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
+    const long li = prm.cu_q ? (long)h * prm.total_q + qs + qrow : ((long)bh * Lq + qrow);
+    prm.LSE[li] = l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
+  }
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -454,15 +542,24 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.Lq + kFwdBM - 1) / kFwdBM;
   const long nblocks = (long)nqt * a.B * a.Hq;
   const float s = a.scale;
+  FwdParams p;
+  p.Q = (const uint16_t*)a.q;
+  p.K = (const uint16_t*)a.k;
+  p.V = (const uint16_t*)a.v;
+  p.O = (uint16_t*)a.o;
+  p.LSE = a.lse;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.B = a.B, p.Hq = a.Hq, p.Hkv = a.Hkv, p.Lq = a.Lq, p.Lk = a.Lk;
+  p.total_q = a.total_q, p.total_k = a.total_k;
+  p.win_left = a.win_left, p.win_right = a.win_right;
   // |scale| * log2(e), kept >= 1e-30 so that masked (-inf) scores always give
   // probability 0; for scale 0 this changes no result beyond 1e-30 relative.
-  const float scale2 = fmaxf(fabsf(s) * kLog2e, 1e-30f);
+  p.scale2 = fmaxf(fabsf(s) * kLog2e, 1e-30f);
   // Rescale threshold of 8 (log2 units) expressed in raw score units.
-  const float thr = 8.f / scale2;
-  const uint32_t qxor = (s < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)nblocks), dim3(kNT), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lq, a.Lk, scale2, thr, qxor);
+  p.thr = 8.f / p.scale2;
+  p.qxor = (s < 0.f) ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)nblocks), dim3(kNT), 0, stream, p);
   return hipGetLastError();
 }
 

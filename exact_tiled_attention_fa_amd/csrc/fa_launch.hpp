@@ -18,6 +18,10 @@ struct FwdArgs {
   float scale;
   int causal;
   int bf16;  // 1: bfloat16, 0: float16
+  int win_left = -1, win_right = -1;  // sliding window, < 0: unbounded side
+  const int* cu_q = nullptr;          // packed sequences (device), or nullptr
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0;       // packed row counts
 };
 
 struct DecodeArgs {

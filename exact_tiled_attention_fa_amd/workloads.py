@@ -14,6 +14,11 @@ Workloads (the numbered configurations of the prefill / decode envelope):
   encoder    B=64 H=12       L=512    D=64  fp16 bidirectional, 1% of key rows x8
   decode     B=128 Hq=32 Hkv=8 D=128 bf16, one query token per sequence,
              cache lengths uniform on [512, 8192], 8 splits
+Structured-mask prefill (sliding window, packed sequences):
+  swa16k     B=2 Hq=32 Hkv=8 L=16384 D=128 bf16 causal, window (4095, 0):
+             each row sees its last 4096 keys (a Mistral-7B-style local window)
+  varlen16   16 packed sequences, lengths uniform on [256, 4096], Hq=32
+             Hkv=8 D=128 bf16 causal (a packed serving prefill batch)
 """
 
 from __future__ import annotations
@@ -78,12 +83,66 @@ class Decode:
         return self.Lk_max or self.len_hi
 
 
+@dataclass(frozen=True)
+class Masked:
+    """Prefill under a structured mask.  Each sequence has equal query and key
+    length.  ``packed`` False: a dense batch of equal lengths; True: the
+    sequences are packed back to back with cumulative offsets."""
+    name: str
+    nseq: int
+    len_lo: int
+    len_hi: int  # inclusive; len_lo == len_hi gives equal lengths
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: torch.dtype
+    causal: bool
+    window: tuple
+    packed: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def lengths(self) -> list:
+        if self.len_lo == self.len_hi:
+            return [self.len_lo] * self.nseq
+        g = _gen(self.seed)
+        return [int(x) for x in torch.randint(self.len_lo, self.len_hi + 1, (self.nseq,),
+                                                  generator=g, dtype=torch.int64)]
+
+    def pairs(self) -> int:
+        """(query, key) pairs the mask allows, summed over the sequences."""
+        left, right = self.window
+        total = 0
+        for n in self.lengths():
+            i = torch.arange(n, dtype=torch.int64)
+            lo = torch.zeros_like(i) if left < 0 else (i - left).clamp(min=0)
+            hi = torch.full_like(i, n - 1)
+            if self.causal:
+                hi = torch.minimum(hi, i)
+            if right >= 0:
+                hi = torch.minimum(hi, i + right)
+            total += int((hi - lo + 1).clamp(min=0).sum())
+        return total
+
+    def flops(self) -> int:
+        return 4 * self.D * self.Hq * self.pairs()
+
+
 PREFILL = {
     "tiny": Prefill("tiny", 1, 2, 2, 128, 64, torch.float16, False, 1),
     "llama7b": Prefill("llama7b", 4, 32, 32, 4096, 128, torch.bfloat16, True, 2),
     "gqa16k": Prefill("gqa16k", 1, 32, 8, 16384, 128, torch.bfloat16, True, 3),
     "d256": Prefill("d256", 2, 16, 16, 4096, 256, torch.float16, True, 31),
     "encoder": Prefill("encoder", 64, 12, 12, 512, 64, torch.float16, False, 4, 0.01, 8.0),
+}
+MASKED = {
+    "swa16k": Masked("swa16k", 2, 16384, 16384, 32, 8, 128, torch.bfloat16, True, (4095, 0),
+                     False, 6),
+    "varlen16": Masked("varlen16", 16, 256, 4096, 32, 8, 128, torch.bfloat16, True, (-1, -1),
+                       True, 7),
 }
 DECODE = {
     "decode": Decode("decode", 128, 32, 8, 128, torch.bfloat16, 512, 8192, 8, 5),
@@ -119,6 +178,27 @@ def randn_qkv(B, Lq, Lk, Hq, Hkv, D, dtype, seed, *, outlier_frac=0.0, outlier_m
 def prefill_inputs(cfg: Prefill):
     return randn_qkv(cfg.B, cfg.L, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, cfg.dtype, cfg.seed,
                      outlier_frac=cfg.outlier_frac, outlier_mult=cfg.outlier_mult)
+
+
+def masked_inputs(cfg: Masked):
+    """Dense: (q [B,L,Hq,D], k, v [B,L,Hkv,D], None).  Packed: (q [total,Hq,D],
+    k, v [total,Hkv,D], cu_seqlens int32 [nseq+1]).  Draw order: the lengths
+    (packed only, from the seed), then Q, K, V as float32 N(0,1) from a
+    generator seeded with seed + 1, then the casts."""
+    lens = cfg.lengths()
+    g = _gen(cfg.seed + 1)
+    if cfg.packed:
+        n = sum(lens)
+        q = torch.randn((n, cfg.Hq, cfg.D), generator=g, dtype=torch.float32)
+        k = torch.randn((n, cfg.Hkv, cfg.D), generator=g, dtype=torch.float32)
+        v = torch.randn((n, cfg.Hkv, cfg.D), generator=g, dtype=torch.float32)
+        cu = torch.tensor([0] + lens, dtype=torch.int64).cumsum(0).to(torch.int32)
+        return q.to(cfg.dtype), k.to(cfg.dtype), v.to(cfg.dtype), cu
+    L = lens[0]
+    q = torch.randn((cfg.nseq, L, cfg.Hq, cfg.D), generator=g, dtype=torch.float32)
+    k = torch.randn((cfg.nseq, L, cfg.Hkv, cfg.D), generator=g, dtype=torch.float32)
+    v = torch.randn((cfg.nseq, L, cfg.Hkv, cfg.D), generator=g, dtype=torch.float32)
+    return q.to(cfg.dtype), k.to(cfg.dtype), v.to(cfg.dtype), None
 
 
 def decode_lengths(cfg: Decode) -> torch.Tensor:

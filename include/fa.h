@@ -52,7 +52,8 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  *               logsumexp (natural log) of the scaled scores over the keys
  *               the row may see.  16-byte aligned.
  *   B, Lq, Lk   >= 1.   Hq, Hkv >= 1 with Hq % Hkv == 0; query head h reads
- *               key/value head h / (Hq / Hkv).
+ *               key/value head h / (Hq / Hkv).  B*Lq*Hq and B*Lk*Hkv must be
+ *               below 2^31 and Hkv*D below 2^25 (FA_ERR_INVALID_ARGUMENT).
  *   D           head dimension: 64, 128 or 256 (others -> FA_ERR_UNSUPPORTED;
  *               the head-dim set of the same page, section 5).
  *   scale       any finite float; scores are scale * q.k.
@@ -67,6 +68,43 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Lq, int Lk, int D, float scale, int causal,
                  fa_dtype dtype, hipStream_t stream);
+
+/*
+ * fa_fwd_ex -- fa_fwd plus structured masks: a sliding window and
+ * block-diagonal packing of several sequences.  The masks are the "local" and
+ * "block-diagonal" structured masks that "5 years, 10K stars: xformers"
+ * (cloud.tencent.com) lists as the way to avoid reading a dense mask; as in
+ * fa_fwd, no mask tensor is read.
+ *
+ *   window_left, window_right
+ *               row i sees keys j with i + (Lk-Lq) - window_left <= j <=
+ *               i + (Lk-Lq) + window_right; a negative value leaves that side
+ *               unbounded.  causal additionally caps j <= i + (Lk-Lq).
+ *               (-1, -1) is no window; (w, 0) with causal=0 equals causal
+ *               attention limited to the last w+1 keys.  A side at least as
+ *               wide as the query plus key rows is the same as unbounded;
+ *               with a window, query plus key rows must be <= 2^30.
+ *   cu_seqlens_q, cu_seqlens_k
+ *               NULL: dense batch, exactly as fa_fwd (q [B,Lq,Hq,D], k/v
+ *               [B,Lk,Hkv,D], lse [B,Hq,Lq]); total_q/total_k are ignored.
+ *               Otherwise device int32 arrays of B+1 non-decreasing offsets
+ *               starting at 0: sequence b is rows cu_seqlens_q[b] ..
+ *               cu_seqlens_q[b+1]-1 of q/o [total_q, Hq, D] and rows
+ *               cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k/v [total_k, Hkv,
+ *               D]; each sequence attends only to its own keys (the causal and
+ *               window rules apply inside it, with its own lengths); lse is
+ *               [Hq, total_q] float32.  Lq and Lk must then be at least the
+ *               longest query / key sequence (rows past Lq of a longer
+ *               sequence are not computed).  Offsets are clamped into
+ *               [0, total] on the device, so inconsistent offsets give wrong
+ *               results but no out-of-bounds access.
+ *   other arguments as in fa_fwd, which is fa_fwd_ex with NULL offsets and
+ *   no window.
+ */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int Lq, int Lk, int total_q, int total_k, int D, float scale, int causal,
+                    int window_left, int window_right, fa_dtype dtype, hipStream_t stream);
 
 /*
  * fa_decode_workspace_size -- bytes of device workspace fa_decode needs for

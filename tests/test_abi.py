@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_decode", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
+        ["fa_fwd", "fa_fwd_ex", "fa_decode", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -114,3 +114,40 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _abi.load()
+
+
+def fwd_ex(**kw):
+    a = dict(q=A16, k=A16, v=A16, o=A16, lse=A16, cu_q=None, cu_k=None, B=1, Hq=2, Hkv=1, Lq=8,
+             Lk=8, total_q=0, total_k=0, D=64, scale=0.125, causal=0, wl=-1, wr=-1,
+             dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_fwd_ex(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(cu_q=A16), _abi.FA_ERR_INVALID_ARGUMENT, "both be set"),
+    (dict(cu_k=A16), _abi.FA_ERR_INVALID_ARGUMENT, "both be set"),
+    (dict(cu_q=A16 + 2, cu_k=A16, total_q=8, total_k=8), _abi.FA_ERR_INVALID_ARGUMENT,
+     "4-byte aligned"),
+    (dict(cu_q=A16, cu_k=A16, total_q=0, total_k=8), _abi.FA_ERR_INVALID_ARGUMENT, "total_q=0"),
+    (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=0), _abi.FA_ERR_INVALID_ARGUMENT, "total_k=0"),
+    (dict(cu_q=A16, cu_k=A16, total_q=1 << 30, total_k=1 << 30, Hq=1, wl=4),
+     _abi.FA_ERR_INVALID_ARGUMENT, "2^30"),
+    (dict(cu_q=A16, cu_k=A16, total_q=1 << 30, total_k=8, Hq=4, Hkv=1),
+     _abi.FA_ERR_INVALID_ARGUMENT, "exceeds 2^31-1"),
+    (dict(Hkv=1 << 20, Hq=1 << 20, D=64), _abi.FA_ERR_INVALID_ARGUMENT, "2^25"),
+    (dict(o=None), _abi.FA_ERR_INVALID_ARGUMENT, "o is NULL"),
+    (dict(D=48), _abi.FA_ERR_UNSUPPORTED, "head_dim 48"),
+])
+def test_fwd_ex_rejects(lib, kw, status, text):
+    assert fwd_ex(**kw) == status
+    assert text in _abi.fa_last_error()
+
+
+def test_fwd_is_fwd_ex_without_masks(lib):
+    """fa_fwd validates exactly as fa_fwd_ex with NULL offsets and no window."""
+    for kw in (dict(B=0), dict(Hq=3, Hkv=2), dict(D=96), dict(scale=float("nan"))):
+        st1 = fwd(**kw)
+        e1 = _abi.fa_last_error()
+        st2 = fwd_ex(**kw)
+        assert (st1, e1) == (st2, _abi.fa_last_error())

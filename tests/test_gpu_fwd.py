@@ -136,3 +136,129 @@ def test_errors_are_raised(gpu):
     k = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16, device=gpu)
     with pytest.raises(FAError, match="FA_ERR_INVALID_ARGUMENT"):
         flash_attn_fwd(q, k, k)
+
+
+# ---------------------------------------------------------------------------
+# Structured masks: sliding windows and block-diagonal packing (fa_fwd_ex).
+# ---------------------------------------------------------------------------
+WINDOWS = [(0, 0), (5, 3), (64, -1), (-1, 40), (127, 0), (300, 300)]
+
+
+@pytest.mark.parametrize("window", WINDOWS, ids=[f"w{a}_{b}" for a, b in WINDOWS])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Lq,Lk", [(300, 300), (129, 331)], ids=["300x300", "129x331"])
+def test_window(Lq, Lk, D, causal, window, gpu):
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd
+
+    dtype = torch.bfloat16 if D != 256 else torch.float16
+    scale = f32(D ** -0.5)
+    q, k, v = W.randn_qkv(1, Lq, Lk, 4, 2, D, dtype, seed=Lq + Lk + D + window[0])
+    tag = f"window {window} Lq={Lq} Lk={Lk} D={D} causal={causal}"
+    say(tag)
+    o, lse = flash_attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), softmax_scale=scale, causal=causal,
+                            window=window)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ref(q, k, v, scale, causal, window=window)
+    compare(o.cpu(), lse.cpu(), o_ref, l_ref, tag)
+
+
+def run_varlen(lens_q, lens_k, Hq, Hkv, D, dtype, causal, window, seed, gpu, heads=None):
+    from exact_tiled_attention_fa_amd.attention import flash_attn_varlen
+
+    cu_q = torch.tensor(np.cumsum([0] + list(lens_q)), dtype=torch.int32)
+    cu_k = torch.tensor(np.cumsum([0] + list(lens_k)), dtype=torch.int32)
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((int(cu_q[-1]), Hq, D), generator=g).to(dtype)
+    k = torch.randn((int(cu_k[-1]), Hkv, D), generator=g).to(dtype)
+    v = torch.randn((int(cu_k[-1]), Hkv, D), generator=g).to(dtype)
+    scale = f32(D ** -0.5)
+    o, lse = flash_attn_varlen(q.to(gpu), k.to(gpu), v.to(gpu), cu_q.to(gpu), cu_k.to(gpu),
+                               max(lens_q), max(lens_k), softmax_scale=scale, causal=causal,
+                               window=window)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.varlen_ref(q, k, v, cu_q, cu_k, scale, causal, window=window, heads=heads)
+    return o.cpu(), lse.cpu(), o_ref, l_ref
+
+
+VARLEN_CASES = [
+    ([1, 130, 0, 257, 64], [5, 130, 3, 300, 64]),   # an empty query sequence
+    ([40, 7, 333], [0, 7, 400]),                    # an empty key sequence: rows see nothing
+    ([128, 128, 128], [128, 128, 128]),
+]
+
+
+@pytest.mark.parametrize("window", [(-1, -1), (32, 8)], ids=["nowin", "win32_8"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("case", range(len(VARLEN_CASES)))
+def test_varlen(case, D, causal, window, gpu):
+    lens_q, lens_k = VARLEN_CASES[case]
+    dtype = torch.float16 if D == 64 else torch.bfloat16
+    tag = f"varlen q={lens_q} k={lens_k} D={D} causal={causal} window={window}"
+    say(tag)
+    o, lse, o_ref, l_ref = run_varlen(lens_q, lens_k, 8, 2, D, dtype, causal, window, 7 * case + D,
+                                      gpu)
+    compare(o, lse, o_ref, l_ref, tag)
+
+
+def test_varlen_equals_dense_batch(gpu):
+    """Equal-length packing gives bit-identical results to the dense batch."""
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd, flash_attn_varlen
+
+    B, L, H, D = 3, 300, 4, 128
+    q, k, v = (t.to(gpu) for t in W.randn_qkv(B, L, L, H, H, D, torch.bfloat16, 55))
+    cu = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device=gpu)
+    for causal in (False, True):
+        o1, l1 = flash_attn_fwd(q, k, v, causal=causal)
+        o2, l2 = flash_attn_varlen(q.reshape(B * L, H, D), k.reshape(B * L, H, D),
+                                   v.reshape(B * L, H, D), cu, cu, L, L, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.reshape(B * L, H, D), o2)
+        assert torch.equal(l1.permute(1, 0, 2).reshape(H, B * L), l2)
+
+
+@pytest.mark.parametrize("name,nheads", [("swa16k", 2), ("varlen16", 6)])
+def test_masked_full_size_sampled(name, nheads, gpu):
+    """The structured-mask workloads at full size, in the launch the benchmark
+    times; the oracle computes a few sampled (sequence, head) slices."""
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd, flash_attn_varlen
+
+    cfg = W.MASKED[name]
+    q, k, v, cu = W.masked_inputs(cfg)
+    lens = cfg.lengths()
+    scale = f32(cfg.scale)
+    rs = np.random.default_rng(cfg.seed)
+    heads = {(0, 0), (cfg.nseq - 1, cfg.Hq - 1)}
+    while len(heads) < nheads:
+        heads.add((int(rs.integers(cfg.nseq)), int(rs.integers(cfg.Hq))))
+    heads = sorted(heads)
+    say(f"{name}: lens={lens} heads={heads}")
+    if cfg.packed:
+        o, lse = flash_attn_varlen(q.to(gpu), k.to(gpu), v.to(gpu), cu.to(gpu), cu.to(gpu),
+                                   max(lens), max(lens), softmax_scale=scale, causal=cfg.causal,
+                                   window=cfg.window)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.varlen_ref(q, k, v, cu, cu, scale, cfg.causal, window=cfg.window,
+                                         heads=heads)
+    else:
+        o, lse = flash_attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), softmax_scale=scale,
+                                causal=cfg.causal, window=cfg.window)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_ref(q, k, v, scale, cfg.causal, window=cfg.window,
+                                            heads=heads)
+    compare(o.cpu(), lse.cpu(), o_ref, l_ref, f"{name} heads={heads}")
+
+
+def test_fwd_ex_errors(gpu):
+    from exact_tiled_attention_fa_amd import _abi
+
+    x = torch.zeros(64, dtype=torch.float32, device=gpu)
+    cu = torch.zeros(4, dtype=torch.int32, device=gpu)
+    p = x.data_ptr()
+    st = _abi.fa_fwd_ex(p, p, p, p, p, cu.data_ptr(), None, 3, 2, 1, 8, 8, 8, 8, 64, 0.1, 0, -1,
+                        -1, _abi.FA_BF16, None)
+    assert st == _abi.FA_ERR_INVALID_ARGUMENT and "both be set" in _abi.fa_last_error()
+    st = _abi.fa_fwd_ex(p, p, p, p, p, cu.data_ptr(), cu.data_ptr(), 3, 2, 1, 8, 8, 0, 8, 64, 0.1,
+                        0, -1, -1, _abi.FA_BF16, None)
+    assert st == _abi.FA_ERR_INVALID_ARGUMENT and "total_q" in _abi.fa_last_error()

@@ -181,3 +181,19 @@ def test_planted_mistake_in_head_mapping_is_caught(name):
     old, new = REF_MUTATIONS[name]
     mutated, _ = _mutant(oatt.attention_ref, old, new)
     assert _rejected(mutated), f"no pin rejects mutant {name}"
+
+
+def test_masked_workload_pair_counts_match_oracle_bounds():
+    """The benchmark's FLOP count for the structured-mask workloads counts
+    exactly the (query, key) pairs the oracle's bounds admit."""
+    from exact_tiled_attention_fa_amd import workloads as W
+
+    for cfg in W.MASKED.values():
+        lens = cfg.lengths()[:3]
+        want = 0
+        for n in lens:
+            lo, hi = oatt.row_bounds(np.arange(n), n, n, cfg.causal, cfg.window)
+            want += int(np.maximum(hi - lo + 1, 0).sum())
+        got = sum(W.Masked(cfg.name, 1, n, n, cfg.Hq, cfg.Hkv, cfg.D, cfg.dtype, cfg.causal,
+                           cfg.window, cfg.packed, cfg.seed).pairs() for n in lens)
+        assert got == want, cfg.name
