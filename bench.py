@@ -53,7 +53,9 @@ def parse():
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--with-copy", type=int, default=0, metavar="MIB",
                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
-    p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--only", choices=["prefill", "decode", "masks"], default=None,
+                   help="masks: time only the structured-mask workloads (one JSON line)")
+    p.add_argument("--mask", default=None, help="time only this structured-mask workload")
     p.add_argument("--no-masks", action="store_true",
                    help="skip the structured-mask prefill workloads (sliding window, packed)")
     p.add_argument("--all-configs", action="store_true",
@@ -61,6 +63,9 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script with "
                         "--with-copy (FETCH_SIZE, then WRITE_SIZE) into profiles/traffic.json")
+    p.add_argument("--pmc-key", default=None,
+                   help="with --summarize-pmc on a run of --only masks --mask NAME: record the "
+                        "forward kernel's traffic under this key (e.g. masks:NAME)")
     return p.parse_args()
 
 
@@ -86,7 +91,7 @@ def traffic_for(kernel: str, digest: str):
     return None
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
+def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> dict:
     """HBM bytes per launch of the prefill and decode kernels from rocprofv3
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same
     counter reads for a plain device copy of copy_mib MiB (reads and writes
@@ -125,11 +130,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
            "copy_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
     f_k, w_k = med(fr, is_fwd), med(wr, is_fwd)
     if f_k is not None and w_k is not None:
-        out["fwd_kernel"] = {"source_digest": source_digest(["fa_fwd.hip", "fa_common.hpp"]),
+        out[key or "fwd_kernel"] = {"source_digest": source_digest(["fa_fwd.hip", "fa_common.hpp"]),
                              "fetch_kib": f_k, "write_kib": w_k,
                              "bytes_per_launch": int((f_k * ff + w_k * fw) * 1024)}
     parts = [(med(fr, p), med(wr, p)) for p in (is_split, is_comb)]
-    if all(a is not None and b is not None for a, b in parts):
+    if key is None and all(a is not None and b is not None for a, b in parts):
         out["decode"] = {"source_digest": source_digest(["fa_decode.hip", "fa_common.hpp"]),
                          "fetch_kib": sum(a for a, _ in parts), "write_kib": sum(b for _, b in parts),
                          "bytes_per_launch": int(sum(a * ff + b * fw for a, b in parts) * 1024)}
@@ -173,6 +178,19 @@ def cpu_baseline_decode(cfg, q, kc, vc, lens, scale, nseq=16):
             "sample": f"first {nseq} of {cfg.B} sequences, all heads, fp64 numpy, {dt:.2f} s wall"}
 
 
+def copy_calibration(mib, dev):
+    """A plain device copy of `mib` MiB, three times: the reference the HBM
+    counters are scaled by."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def time_masked(cfg, dev, reps=10, warmup=3):
     """Mean launch time (ms, HIP events on the launch stream) of one
     structured-mask workload, and its algorithmic TFLOP/s."""
@@ -208,6 +226,7 @@ def time_masked(cfg, dev, reps=10, warmup=3):
     mean = float(np.mean(ms))
     tf = cfg.flops() / (mean * 1e-3) / 1e12
     lens = cfg.lengths()
+    traffic = traffic_for(f"masks:{cfg.name}", source_digest(["fa_fwd.hip", "fa_common.hpp"]))
     return {"workload": f"{cfg.nseq} x L={'%d' % lens[0] if cfg.len_lo == cfg.len_hi else 'U[%d,%d]' % (cfg.len_lo, cfg.len_hi)}"
                         f" Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} {str(cfg.dtype)[6:]}"
                         f" causal={cfg.causal} window={tuple(cfg.window)}"
@@ -215,17 +234,27 @@ def time_masked(cfg, dev, reps=10, warmup=3):
             "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
                    "min": round(float(np.min(ms)), 5)},
             "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3), "unit": "TFLOP/s",
+            "alg_bytes_per_launch": cfg.hbm_bytes(),
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                         "traffic": traffic},
+            "kernel": "fwd_kernel<bf16_t, 128, true>"}
 
 
 def main():
     args = parse()
     if args.summarize_pmc:
-        t = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.with_copy or 1024)
+        t = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.with_copy or 1024,
+                          args.pmc_key)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        try:
+            with open(TRAFFIC_FILE) as f:
+                merged = json.load(f)
+        except (OSError, ValueError):
+            merged = {}
+        merged.update(t)
         with open(TRAFFIC_FILE, "w") as f:
-            json.dump(t, f, indent=1)
+            json.dump(merged, f, indent=1)
         print(json.dumps(t))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -244,6 +273,14 @@ def main():
     info = _abi.fa_info()
     do_pf = args.only in (None, "prefill")
     do_dec = args.only in (None, "decode")
+    masks = {n: c for n, c in W.MASKED.items() if args.mask in (None, n)}
+    if args.only == "masks":
+        print("# structured-mask workloads", file=sys.stderr, flush=True)
+        res = {n: time_masked(c, dev) for n, c in masks.items()}
+        if args.with_copy:
+            copy_calibration(args.with_copy, dev)
+        print(json.dumps({"masks": res, "lib": info}), flush=True)
+        return
 
     pcfg = W.PREFILL["llama7b"]
     dcfg = W.DECODE["decode"]
@@ -292,12 +329,7 @@ def main():
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
 
     if args.with_copy:
-        n = args.with_copy * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration(args.with_copy, dev)
 
     out = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
@@ -341,7 +373,7 @@ def main():
             out["value"], out["unit"] = round(gbs, 2), "GB/s"
     if do_pf and not args.no_masks:
         print("# structured-mask workloads", file=sys.stderr, flush=True)
-        out["masks"] = {name: time_masked(cfg, dev) for name, cfg in W.MASKED.items()}
+        out["masks"] = {name: time_masked(cfg, dev) for name, cfg in masks.items()}
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         if do_pf:

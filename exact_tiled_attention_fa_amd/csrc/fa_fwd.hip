@@ -151,20 +151,26 @@ void fwd_kernel(const FwdParams prm) {
   // XCD x takes query heads [x*Hq/8, (x+1)*Hq/8) of every sequence (the heads
   // that share a K/V head are adjacent, so they land together), which keeps
   // the XCDs balanced even when packed sequences differ in length.
+  // Within an XCD the items go sequence by sequence, then by runs of gx
+  // adjacent heads that share a K/V head (gx = gcd(Hq/Hkv, Hq/8)), then
+  // heaviest query tile first, the run's heads innermost: the heads reading
+  // one K/V tile run at the same time and share it in L2.
   // Otherwise XCD x takes the x-th contiguous slice of the (batch, head,
-  // query tile) list.  Either way an XCD walks its items sequence by sequence,
-  // head by head, heaviest query tile first.
+  // query tile) list.
   const int nqt = (prm.Lq + BM - 1) / BM;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   int b, h, qt;
   if (Hq % kXcds == 0) {
     const int hx = Hq / kXcds;
+    int gx = Hq / Hkv, m = hx;  // gx = gcd(group size, hx)
+    while (m != 0) { const int t = gx % m; gx = m; m = t; }
     const int per_b = hx * nqt;
     b = slot / per_b;
     const int r = slot - b * per_b;
-    const int hh = r / nqt;
-    qt = r - hh * nqt;
-    h = xcd * hx + hh;
+    const int run = r / (nqt * gx);
+    const int r2 = r - run * (nqt * gx);
+    qt = r2 / gx;
+    h = xcd * hx + run * gx + (r2 - qt * gx);
   } else {
     const int N = nqt * B * Hq;
     const int item = xcd * (N / kXcds) + min(xcd, N % kXcds) + slot;

@@ -130,6 +130,12 @@ class Masked:
     def flops(self) -> int:
         return 4 * self.D * self.Hq * self.pairs()
 
+    def hbm_bytes(self) -> int:
+        """Algorithmic bytes: Q, K, V read once; O and lse written once."""
+        n = sum(self.lengths())
+        e = 2
+        return 2 * n * self.Hq * self.D * e + 2 * n * self.Hkv * self.D * e + n * self.Hq * 4
+
 
 PREFILL = {
     "tiny": Prefill("tiny", 1, 2, 2, 128, 64, torch.float16, False, 1),
