@@ -197,3 +197,27 @@ def test_masked_workload_pair_counts_match_oracle_bounds():
         got = sum(W.Masked(cfg.name, 1, n, n, cfg.Hq, cfg.Hkv, cfg.D, cfg.dtype, cfg.causal,
                            cfg.window, cfg.packed, cfg.seed).pairs() for n in lens)
         assert got == want, cfg.name
+
+
+def test_varlen_empty_sequences_and_isolation():
+    """An empty key sequence leaves its rows O = 0, lse = -inf; an empty query
+    sequence yields no rows; changing one sequence's K/V changes no other
+    sequence's output."""
+    r = np.random.default_rng(19)
+    lens_q, lens_k = [2, 0, 3, 4], [0, 3, 3, 5]
+    cu_q, cu_k = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    q = r.standard_normal((cu_q[-1], 2, 4))
+    k = r.standard_normal((cu_k[-1], 1, 4))
+    v = r.standard_normal((cu_k[-1], 1, 4))
+    for causal, win in ((False, (-1, -1)), (True, (-1, -1)), (True, (1, -1))):
+        o, l = oracle.varlen_ref(q, k, v, cu_q, cu_k, 0.6, causal, window=win)
+        assert np.all(o[0:2] == 0.0) and np.all(np.isneginf(l[:, 0:2]))
+        assert np.all(np.isfinite(o[2:])) and np.all(np.isfinite(l[:, 2:]))
+        k2, v2 = k.copy(), v.copy()
+        k2[cu_k[2]:cu_k[3]] += 3.0   # sequence 2's keys and values only
+        v2[cu_k[2]:cu_k[3]] *= -2.0
+        o2, l2 = oracle.varlen_ref(q, k2, v2, cu_q, cu_k, 0.6, causal, window=win)
+        seq2 = slice(cu_q[2], cu_q[3])
+        assert not np.allclose(o2[seq2], o[seq2])
+        keep = np.r_[0:cu_q[2], cu_q[3]:cu_q[-1]]
+        assert np.array_equal(o2[keep], o[keep]) and np.array_equal(l2[:, keep], l[:, keep])
