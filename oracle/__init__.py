@@ -18,6 +18,9 @@ Contents
 ``attention.decode_ref``
     The same definition for one query token per sequence against a padded
     KV cache with per-sequence lengths.
+``attention.decode_paged_ref``
+    Decode against a paged KV cache (page table per sequence), optionally
+    with int8 keys and/or values carrying one scale per cached row.
 ``online.online_attention_ref`` / ``online.split_combine_ref``
     The blockwise online-softmax recurrence and the logsumexp merge of
     key-chunk summaries, restated in float64 from the pages.  These are
@@ -29,12 +32,14 @@ than itself: a 40-digit ``decimal`` brute force, PyTorch's fp64 CPU
 ``scaled_dot_product_attention``, closed forms and invariants.
 """
 
-from .attention import attention_ref, causal_allowed, decode_ref, key_bounds, varlen_ref
+from .attention import (attention_ref, causal_allowed, decode_paged_ref, decode_ref, key_bounds,
+                        varlen_ref)
 from .online import online_attention_ref, split_combine_ref
 
 __all__ = [
     "attention_ref",
     "decode_ref",
+    "decode_paged_ref",
     "causal_allowed",
     "key_bounds",
     "varlen_ref",

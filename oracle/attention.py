@@ -45,6 +45,16 @@ Sources (page title, section):
   additionally caps j <= i + shift); and block-diagonal packing as sequences
   given by cumulative offsets cu_q / cu_k, each attending only to itself.
 
+* "FlashAttention-2 (TH)" (systems-analysis.info), references, cite
+  PagedAttention: a KV cache kept in fixed-size pages reached through a
+  per-sequence page table.  Read here as pages [num_pages, P, Hkv, D] and a
+  table [B, max_pages]: key j of sequence b is slot j % P of page
+  table[b, j // P].
+* "MNN LLM attention_mode" (lpnh.cn), encoding section: KV-cache modes with
+  the keys, or the keys and the values, stored as int8.  The page gives no
+  quantiser; read here as a symmetric int8 code with one float scale per
+  cached row (page, slot, kv head), the cached value being code * scale.
+
 Implementation notes: each (b, h) pair is independent; rows are processed in
 blocks of ``row_block`` so that at most row_block x Lk scores exist at once.
 That is still the plain definition -- each row's max, sum and weighted sum run
@@ -216,6 +226,59 @@ def decode_ref(q, k_cache, v_cache, seqlens, scale: float, *, heads=None):
             cache_v[key] = _as_f64(v_cache[b, :n, kv, :])
         o, l = _head_attention(q[b, h, :][None, :], cache_k[key], cache_v[key],
                                float(scale), False, 1)
+        out[b, h, :] = o[0]
+        lse[b, h] = l[0]
+    return out, lse
+
+
+def _paged_rows(pages, scales, rows_page, rows_slot, kv):
+    """Cached rows (page, slot, kv head) as float64, times their scales."""
+    if hasattr(pages, "detach"):  # torch: index before converting
+        import torch
+
+        ip, isl = torch.as_tensor(rows_page), torch.as_tensor(rows_slot)
+        x = _as_f64(pages[ip, isl, kv])
+        sc = None if scales is None else _as_f64(scales[ip, isl, kv])
+    else:
+        x = _as_f64(np.asarray(pages)[rows_page, rows_slot, kv])
+        sc = None if scales is None else _as_f64(np.asarray(scales)[rows_page, rows_slot, kv])
+    return x if sc is None else x * sc[:, None]
+
+
+def decode_paged_ref(q, k_pages, v_pages, block_table, seqlens, scale: float, *, k_scales=None,
+                     v_scales=None, heads=None):
+    """One query token per sequence against a paged, optionally int8, cache.
+
+    q: [B, Hq, D]; k_pages, v_pages: [num_pages, P, Hkv, D]; block_table:
+    [B, max_pages] page numbers; seqlens: [B].  Key j of sequence b is slot
+    j % P of page block_table[b, j // P]; sequence b sees keys 0 ..
+    min(seqlens[b], max_pages * P) - 1.  With k_scales ([num_pages, P, Hkv])
+    k_pages holds integer codes and the cached key is code * scale (exact in
+    float64); likewise v_scales for the values.  Then the definition of
+    ``decode_ref``.  Returns (O [B, Hq, D], lse [B, Hq]) in float64.
+    """
+    q = _as_f64(q)
+    B, Hq, D = q.shape
+    P, Hkv = int(k_pages.shape[1]), int(k_pages.shape[2])
+    bt = np.asarray(block_table).astype(np.int64).reshape(B, -1)
+    lens = [int(x) for x in np.asarray(seqlens).reshape(-1)]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    out = np.full((B, Hq, int(v_pages.shape[3])), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    jobs = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    cache = {}
+    for b, h in jobs:
+        kv = h // g
+        if (b, kv) not in cache:
+            n = max(0, min(lens[b], bt.shape[1] * P))
+            j = np.arange(n)
+            page, slot = bt[b, j // P], j % P
+            cache[(b, kv)] = (_paged_rows(k_pages, k_scales, page, slot, kv),
+                              _paged_rows(v_pages, v_scales, page, slot, kv))
+        kb, vb = cache[(b, kv)]
+        o, l = _head_attention(q[b, h, :][None, :], kb, vb, float(scale), False, 1)
         out[b, h, :] = o[0]
         lse[b, h] = l[0]
     return out, lse
