@@ -53,8 +53,13 @@ def parse():
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--with-copy", type=int, default=0, metavar="MIB",
                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
-    p.add_argument("--only", choices=["prefill", "decode", "masks"], default=None,
-                   help="masks: time only the structured-mask workloads (one JSON line)")
+    p.add_argument("--only", choices=["prefill", "decode", "masks", "paged"], default=None,
+                   help="masks / paged: time only the structured-mask prefill or the paged "
+                        "decode workloads (one JSON line)")
+    p.add_argument("--paged-format", choices=["native", "k8", "kv8"], default=None,
+                   help="time only this paged-cache format")
+    p.add_argument("--no-paged", action="store_true",
+                   help="skip the paged-cache decode workloads")
     p.add_argument("--mask", default=None, help="time only this structured-mask workload")
     p.add_argument("--no-masks", action="store_true",
                    help="skip the structured-mask prefill workloads (sliding window, packed)")
@@ -115,7 +120,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> di
 
     is_copy = lambda n: "copybuffer" in n.lower()  # the runtime's device-to-device copy kernel
     is_fwd = lambda n: "fwd_kernel<fa::bf16_t, 128, true>" in n
-    is_split = lambda n: "decode_split_kernel<fa::bf16_t, 128>" in n
+    is_split = lambda n: "decode_split_kernel<fa::bf16_t, 128," in n  # one cache format per run
     is_comb = lambda n: "decode_combine_kernel<fa::bf16_t, 128>" in n
     fr, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
     kib = copy_mib * 1024.0
@@ -129,13 +134,14 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> di
                      f"plain {copy_mib} MiB device copy read and write exactly {copy_mib} MiB.",
            "copy_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
     f_k, w_k = med(fr, is_fwd), med(wr, is_fwd)
-    if f_k is not None and w_k is not None:
+    if f_k is not None and w_k is not None and not (key or "").startswith("paged:"):
         out[key or "fwd_kernel"] = {"source_digest": source_digest(["fa_fwd.hip", "fa_common.hpp"]),
                              "fetch_kib": f_k, "write_kib": w_k,
                              "bytes_per_launch": int((f_k * ff + w_k * fw) * 1024)}
     parts = [(med(fr, p), med(wr, p)) for p in (is_split, is_comb)]
-    if key is None and all(a is not None and b is not None for a, b in parts):
-        out["decode"] = {"source_digest": source_digest(["fa_decode.hip", "fa_common.hpp"]),
+    if all(a is not None and b is not None for a, b in parts) and (key is None or
+                                                                  key.startswith("paged:")):
+        out[key or "decode"] = {"source_digest": source_digest(["fa_decode.hip", "fa_common.hpp"]),
                          "fetch_kib": sum(a for a, _ in parts), "write_kib": sum(b for _, b in parts),
                          "bytes_per_launch": int(sum(a * ff + b * fw for a, b in parts) * 1024)}
     return out
@@ -189,6 +195,58 @@ def copy_calibration(mib, dev):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
+
+
+PAGED_FORMATS = {"native": (False, False), "k8": (True, False), "kv8": (True, True)}
+PAGE_SIZE = 16
+
+
+def time_paged(fmt, dev, reps=10, warmup=3):
+    """The decode workload in a paged cache of 16-slot pages (native, int8
+    keys, or int8 keys and values): mean time of fa_decode_paged (split +
+    combine, HIP events on the launch stream) and algorithmic GB/s."""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import decode_workspace, flash_attn_decode_paged
+
+    cfg = W.DECODE["decode"]
+    k8, v8 = PAGED_FORMATS[fmt]
+    q, kp, vp, ks, vs, table, lens = W.paged_decode_inputs(cfg, PAGE_SIZE, k_int8=k8, v_int8=v8)
+    to = lambda t: None if t is None else t.to(dev)
+    q, kp, vp, ks, vs, table, lens_d = (to(t) for t in (q, kp, vp, ks, vs, table, lens))
+    ws = decode_workspace(cfg.B, cfg.Hq, cfg.D, cfg.num_splits, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device=dev)
+    sc = float(np.float32(cfg.scale))
+    run = lambda: flash_attn_decode_paged(q, kp, vp, table, lens_d, k_scales=ks, v_scales=vs,
+                                          softmax_scale=sc, num_splits=cfg.num_splits,
+                                          workspace=ws, out=o, lse=lse)
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    mean = float(np.mean(ms))
+    byts = W.paged_decode_bytes(cfg, lens, PAGE_SIZE, k_int8=k8, v_int8=v8)
+    gbs = byts / (mean * 1e-3) / 1e9
+    traffic = traffic_for(f"paged:{fmt}", source_digest(["fa_decode.hip", "fa_common.hpp"]))
+    return {"workload": f"decode workload in {PAGE_SIZE}-slot pages, keys "
+                        f"{'int8' if k8 else 'bf16'}, values {'int8' if v8 else 'bf16'}",
+            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
+                   "min": round(float(np.min(ms)), 5)},
+            "alg_bytes_per_step": byts, "value": round(gbs, 2), "unit": "GB/s",
+            "tokens_per_s": round(cfg.B / (mean * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic}}
 
 
 def time_masked(cfg, dev, reps=10, warmup=3):
@@ -274,6 +332,14 @@ def main():
     do_pf = args.only in (None, "prefill")
     do_dec = args.only in (None, "decode")
     masks = {n: c for n, c in W.MASKED.items() if args.mask in (None, n)}
+    paged_fmts = [f for f in PAGED_FORMATS if args.paged_format in (None, f)]
+    if args.only == "paged":
+        print("# paged decode workloads", file=sys.stderr, flush=True)
+        res = {f: time_paged(f, dev) for f in paged_fmts}
+        if args.with_copy:
+            copy_calibration(args.with_copy, dev)
+        print(json.dumps({"paged": res, "lib": info}), flush=True)
+        return
     if args.only == "masks":
         print("# structured-mask workloads", file=sys.stderr, flush=True)
         res = {n: time_masked(c, dev) for n, c in masks.items()}
@@ -371,6 +437,9 @@ def main():
                                           ["fa_decode.hip", "fa_common.hpp"]))}}
         if out["value"] is None:
             out["value"], out["unit"] = round(gbs, 2), "GB/s"
+    if do_dec and not args.no_paged:
+        print("# paged decode workloads", file=sys.stderr, flush=True)
+        out["decode"]["paged"] = {f: time_paged(f, dev) for f in paged_fmts}
     if do_pf and not args.no_masks:
         print("# structured-mask workloads", file=sys.stderr, flush=True)
         out["masks"] = {name: time_masked(cfg, dev) for name, cfg in masks.items()}

@@ -7,26 +7,28 @@ synthetic input generators.
 """
 
 from . import _abi
-from ._abi import (fa_decode, fa_decode_workspace_size, fa_fwd, fa_fwd_ex, fa_info,
-                   fa_last_error)
+from ._abi import (fa_decode, fa_decode_paged, fa_decode_workspace_size, fa_fwd, fa_fwd_ex,
+                   fa_info, fa_last_error)
 
 __all__ = [
     "fa_fwd",
     "fa_fwd_ex",
     "fa_decode",
+    "fa_decode_paged",
     "fa_decode_workspace_size",
     "fa_info",
     "fa_last_error",
     "flash_attn_fwd",
     "flash_attn_decode",
+    "flash_attn_decode_paged",
     "flash_attn_varlen",
     "decode_workspace",
 ]
 
 
 def __getattr__(name):  # torch-facing wrappers are imported lazily
-    if name in ("flash_attn_fwd", "flash_attn_varlen", "flash_attn_decode", "decode_workspace",
-                "FAError"):
+    if name in ("flash_attn_fwd", "flash_attn_varlen", "flash_attn_decode",
+                "flash_attn_decode_paged", "decode_workspace", "FAError"):
         from . import attention
 
         return getattr(attention, name)

@@ -19,6 +19,9 @@ FA_ERR_HIP = 3
 FA_F16 = 0
 FA_BF16 = 1
 
+FA_KV_NATIVE = 0
+FA_KV_INT8 = 1
+
 STATUS_NAMES = {
     FA_OK: "FA_OK",
     FA_ERR_INVALID_ARGUMENT: "FA_ERR_INVALID_ARGUMENT",
@@ -37,6 +40,8 @@ SIGNATURES = {
                        _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
+    "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                             _I, _I, _I, _P, _Z, _I, _P]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_info": (ctypes.c_char_p, []),
 }
@@ -90,6 +95,15 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale
               workspace, workspace_bytes, dtype, stream) -> int:
     return load().fa_decode(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale,
                             num_splits, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_decode_paged(q, k_pages, v_pages, k_scales, v_scales, block_table, seqlens, o, lse, B, Hq,
+                    Hkv, D, num_pages, page_size, max_pages, scale, num_splits, k_format, v_format,
+                    workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_decode_paged(q, k_pages, v_pages, k_scales, v_scales, block_table, seqlens, o,
+                                  lse, B, Hq, Hkv, D, num_pages, page_size, max_pages, scale,
+                                  num_splits, k_format, v_format, workspace, workspace_bytes,
+                                  dtype, stream)
 
 
 def fa_last_error() -> str:

@@ -161,3 +161,60 @@ def flash_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if st != _abi.FA_OK:
         raise FAError(st, "fa_decode")
     return out, lse
+
+
+def flash_attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                            block_table: torch.Tensor, seqlens: torch.Tensor, *, k_scales=None,
+                            v_scales=None, softmax_scale=None, num_splits: int = 8,
+                            workspace=None, out=None, lse=None):
+    """Decode against a paged cache.  q [B,Hq,D]; k_pages, v_pages
+    [num_pages, page_size, Hkv, D] in q's dtype, or int8 codes with float32
+    scales [num_pages, Hkv, page_size] in k_scales / v_scales; block_table
+    int32 [B, max_pages]; seqlens int32 [B].  Returns (o [B,Hq,D], lse [B,Hq])."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                 (seqlens, "seqlens")):
+        _check_dev(t, n)
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("expected q [B,Hq,D] and k_pages, v_pages [num_pages,page_size,Hkv,D]")
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be float16 or bfloat16")
+    fmts = []
+    for pages, sc, n in ((k_pages, k_scales, "k"), (v_pages, v_scales, "v")):
+        if pages.dtype == torch.int8:
+            if sc is None:
+                raise ValueError(f"{n}_pages is int8: {n}_scales is required")
+            _check_dev(sc, f"{n}_scales")
+            want = (pages.shape[0], pages.shape[2], pages.shape[1])
+            if sc.dtype != torch.float32 or tuple(sc.shape) != want:
+                raise ValueError(f"{n}_scales must be float32 [num_pages, Hkv, page_size]")
+            fmts.append(_abi.FA_KV_INT8)
+        elif pages.dtype == q.dtype:
+            fmts.append(_abi.FA_KV_NATIVE)
+        else:
+            raise ValueError(f"{n}_pages must be int8 or q's dtype")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or block_table.shape[0] != B:
+        raise ValueError("head_dim or batch mismatch")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+        raise ValueError("seqlens must be int32 [B]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, D, num_splits, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = _abi.fa_decode_paged(
+        q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+        k_scales.data_ptr() if fmts[0] == _abi.FA_KV_INT8 else None,
+        v_scales.data_ptr() if fmts[1] == _abi.FA_KV_INT8 else None,
+        block_table.data_ptr(), seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, D,
+        num_pages, page_size, block_table.shape[1], scale, num_splits, fmts[0], fmts[1],
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _DTYPES[q.dtype],
+        _stream_handle(q.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_decode_paged")
+    return out, lse

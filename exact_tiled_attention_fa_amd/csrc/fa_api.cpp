@@ -161,6 +161,78 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
   return ok();
 }
 
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const float* k_scales, const float* v_scales, const int* block_table,
+                          const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv, int D,
+                          int num_pages, int page_size, int max_pages, float scale,
+                          int num_splits, fa_kv_format k_format, fa_kv_format v_format,
+                          void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                          hipStream_t stream) {
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k_pages, "k_pages"));
+  FA_TRY(check_ptr(v_pages, "v_pages"));
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(lse, "lse"));
+  FA_TRY(check_ptr(workspace, "workspace"));
+  if (!block_table) return fail(FA_ERR_INVALID_ARGUMENT, "block_table is NULL");
+  if (!seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "seqlens is NULL");
+  if (((uintptr_t)block_table & 3u) || ((uintptr_t)seqlens & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_table and seqlens must be 4-byte aligned");
+  if ((k_format != FA_KV_NATIVE && k_format != FA_KV_INT8) ||
+      (v_format != FA_KV_NATIVE && v_format != FA_KV_INT8))
+    return fail(FA_ERR_UNSUPPORTED, "kv formats %d/%d are not FA_KV_NATIVE or FA_KV_INT8",
+                (int)k_format, (int)v_format);
+  if (k_format == FA_KV_NATIVE && v_format == FA_KV_INT8)
+    return fail(FA_ERR_UNSUPPORTED, "int8 values need int8 keys");
+  const bool k8 = k_format == FA_KV_INT8, v8 = v_format == FA_KV_INT8;
+  if (k8 && (!k_scales || !aligned16(k_scales)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "k_scales must be a 16-byte aligned pointer for int8 keys");
+  if (v8 && (!v_scales || !aligned16(v_scales)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "v_scales must be a 16-byte aligned pointer for int8 values");
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || num_pages < 1 || max_pages < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "sizes must be >= 1 (B=%d Hq=%d Hkv=%d D=%d num_pages=%d max_pages=%d)", B, Hq,
+                Hkv, D, num_pages, max_pages);
+  if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "page_size=%d is not a power of two in [16, 65536]",
+                page_size);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (num_splits < 1 || num_splits > 64)
+    return fail(FA_ERR_INVALID_ARGUMENT, "num_splits=%d not in [1, 64]", num_splits);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)dtype);
+  if (!head_dim_supported(D))
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", D);
+  if ((long long)max_pages * page_size > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "max_pages * page_size exceeds 2^31-1");
+  if ((long long)B * max_pages > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B * max_pages exceeds 2^31-1");
+  if ((long long)Hkv * ((Hq / Hkv + 15) / 16) > 65535 || B > 65535)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (B or Hq exceeds 65535)");
+  const size_t need = fa::decode_workspace_bytes(B, Hq, D, num_splits);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                need);
+
+  fa::DecodeArgs a{q, k_pages, v_pages, seqlens, o, lse, B, Hq, Hkv, 0, D, scale,
+                   num_splits, workspace, dtype == FA_BF16 ? 1 : 0};
+  a.paged = 1;
+  a.block_table = block_table;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.k_int8 = k8 ? 1 : 0;
+  a.v_int8 = v8 ? 1 : 0;
+  a.k_scales = k8 ? k_scales : nullptr;
+  a.v_scales = v8 ? v_scales : nullptr;
+  hipError_t e = fa::launch_decode(a, stream);
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "fa_decode_paged launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* fa_last_error(void) { return g_err; }
 
 const char* fa_info(void) {
@@ -169,7 +241,8 @@ const char* fa_info(void) {
          "mfma_f32_32x32x16, LDS-direct K/V with transpose reads, causal/window tile "
          "skip, block-diagonal packing, GQA; "
          "decode: split-KV, 4 wave64 per (chunk, kv head, 16 heads, sequence), 16-key steps, "
-         "mfma_f32_16x16x32 + 16x16x16, logsumexp combine; version=0.2.0";
+         "mfma_f32_16x16x32 + 16x16x16, logsumexp combine, paged and int8 KV caches; "
+         "version=0.3.0";
 }
 
 }  // extern "C"

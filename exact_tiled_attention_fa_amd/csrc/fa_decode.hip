@@ -28,6 +28,20 @@
 // At the end the four waves' (O, lse) are merged through LDS.  Workspace:
 // float32 partial outputs [B, Hq, S, D], then float32 partial logsumexps in
 // base 2 [B, Hq, S].
+//
+// Paged and int8 caches (the PagedAttention reference of "FlashAttention-2
+// (TH)" (systems-analysis.info), references; the KV-INT8 modes of "MNN LLM
+// attention_mode" (lpnh.cn), encoding section).  A paged cache keeps rows in
+// pages of P slots; key j of sequence b is slot j % P of page table[b, j / P].
+// Chunks are then rounded up to whole 16-key steps and P is a power of two
+// >= 16, so each step lies in one page and needs one table entry (a scalar
+// load).  An int8 side holds codes with one float scale per cached row: key
+// codes are widened exactly to the 16-bit type for the MFMA and the row's
+// scale multiplies its scores; value codes are widened exactly when the V
+// tile is written to LDS and the row's scale multiplies its probability
+// before the 16-bit rounding (the row sum uses the unscaled probabilities).
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -35,6 +49,7 @@ namespace fa {
 namespace {
 
 constexpr int kKS = kDecodeKeysPerStep;  // keys per step (one 16-key MFMA block)
+
 constexpr int kDW = 4;                   // waves per split workgroup
 static_assert(kKS == 16, "the decode MFMA layout assumes 16-key steps");
 
@@ -44,15 +59,48 @@ template <int D> __device__ __forceinline__ int swz_dv(int r) {
   return D == 64 ? 2 * ((r >> 1) & 3) : 2 * (r & 7);
 }
 
-template <typename T, int D>
+struct SplitParams {
+  const uint16_t* Q;
+  const void* K;  // dense [B, Lmax, Hkv, D]; paged [num_pages, P, Hkv, D]; 16-bit or int8
+  const void* V;
+  const float* ksc;  // int8 keys: scales [num_pages, Hkv, P]
+  const float* vsc;  // int8 values: scales [num_pages, Hkv, P]
+  const int* table;  // paged: [B, max_pages]
+  const int* seqlens;
+  float* Opart;
+  float* Lpart;
+  int Hq, Hkv;
+  int Lmax;  // longest sequence the cache holds (paged: max_pages * P)
+  int page_shift, max_pages, num_pages;
+  int S;
+  float scale2, thr;
+  uint32_t qxor;
+};
+
+// Eight int8 codes (two dwords) widened exactly to eight 16-bit values.
+template <typename T> __device__ __forceinline__ u32x4 widen8(u32x2 x) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = x[i >> 1] >> (16 * (i & 1));
+    r[i] = Ops<T>::pack2((float)(int8_t)(w & 0xffu), (float)(int8_t)((w >> 8) & 0xffu));
+  }
+  return r;
+}
+
+template <typename T, int D, bool PAGED, bool KI8, bool VI8>
 __global__ __launch_bounds__(64 * kDW)
-void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
-                         const uint16_t* __restrict__ Vc, const int* __restrict__ seqlens,
-                         float* __restrict__ Opart, float* __restrict__ Lpart, int Hq, int Hkv,
-                         int Lmax, int S, float scale2, float thr, uint32_t qxor) {
+void decode_split_kernel(const SplitParams prm) {
+  const int Hq = prm.Hq, Hkv = prm.Hkv, Lmax = prm.Lmax, S = prm.S;
+  const float scale2 = prm.scale2, thr = prm.thr;
+  const uint32_t qxor = prm.qxor;
+  const uint16_t* __restrict__ Q = prm.Q;
+  float* __restrict__ Opart = prm.Opart;
+  float* __restrict__ Lpart = prm.Lpart;
   constexpr int CPR = D / 8;
   constexpr int VT = kKS * D;          // elements per V tile
-  constexpr int NVL = kKS * CPR / 64;  // 16-byte V (and K) loads per lane per step
+  // 16-byte V loads per lane per step (8 16-bit or 16 int8 elements each)
+  constexpr int NVL = VI8 ? kKS * D / 16 / 64 : kKS * CPR / 64;
   constexpr int MERGE = 16 * D * 2;    // per-wave merge room in elements (16 heads x D floats)
   constexpr int WS = VT > MERGE ? VT : MERGE;
   __shared__ __attribute__((aligned(16))) uint16_t sV[kDW][WS];
@@ -70,9 +118,10 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  int len = seqlens[b];
+  int len = prm.seqlens[b];
   len = len < 0 ? 0 : (len > Lmax ? Lmax : len);
-  const int C = (len + S - 1) / S;
+  int C = (len + S - 1) / S;
+  if (PAGED) C = (C + kKS - 1) / kKS * kKS;  // whole steps: a step never straddles a page
   const int k0 = split * C;
   const int k1 = min(len, k0 + C);
   const long pbase = ((long)b * Hq + kvh * g + hg * 16) * S + split;  // partial of head slot 0
@@ -95,36 +144,96 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     qf[ks] = hvalid ? x : (u32x4){0u, 0u, 0u, 0u};
   }
 
-  const long kstride = (long)Hkv * D;
-  const uint16_t* Kb = Kc + (long)b * Lmax * kstride + (long)kvh * D;
-  const uint16_t* Vb = Vc + (long)b * Lmax * kstride + (long)kvh * D;
+  const long kstride = (long)Hkv * D;  // elements from one cached row to the next
+  using KE = std::conditional_t<KI8, int8_t, uint16_t>;
+  using VE = std::conditional_t<VI8, int8_t, uint16_t>;
+  const KE* Kb = static_cast<const KE*>(prm.K) + (long)kvh * D;
+  const VE* Vb = static_cast<const VE*>(prm.V) + (long)kvh * D;
+  if (!PAGED) {
+    Kb += (long)b * Lmax * kstride;
+    Vb += (long)b * Lmax * kstride;
+  }
 
   const int nsteps = (k1 - k0 + kKS - 1) / kKS;
   const int my_steps = nsteps > w ? (nsteps - w + kDW - 1) / kDW : 0;
 
-  // Keys past the chunk end are redirected to its last key (finite data;
-  // their scores are masked), so padding rows are never read.
-  auto kload = [&](int j, u32x4 (&kx)[D / 32]) {
-    const int key = min(k0 + kKS * j + l16, k1 - 1);
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) kx[ks] = load16(Kb + (long)key * kstride + 32 * ks + 8 * q4);
+  // Step j covers keys k0 + 16j .. +15.  `first` is its first key (a step
+  // past the chunk's end maps onto the chunk's last step, whose rows are
+  // re-read), row0 the cache row of that key (key first + i lives in row
+  // row0 + i) and srow the index of its scale (paged int8).  Keys past the
+  // chunk end are redirected to its last key (finite data; their scores are
+  // masked), so padding is never read.
+  struct StepRows { int first; long row0; long srow; };
+  // Paged: a window of 64 table entries in a VGPR (lane i holds the entry of
+  // page wstart + i), refilled when a step leaves it, so the page of a step
+  // is a readlane rather than a dependent memory load.
+  int wstart = -(1 << 30), vtab = 0;
+  auto step_rows = [&](int j) -> StepRows {
+    if constexpr (PAGED) {
+      const int first = min(k0 + kKS * j, (k1 - 1) & ~(kKS - 1));
+      const int pg = first >> prm.page_shift;
+      if (pg < wstart || pg >= wstart + 64) {
+        wstart = pg;
+        const int e = min(pg + lane, prm.max_pages - 1);
+        vtab = min(max(prm.table[(long)b * prm.max_pages + e], 0), prm.num_pages - 1);
+      }
+      const long phys = __builtin_amdgcn_readlane(vtab, pg - wstart);
+      const int slot = first & ((1 << prm.page_shift) - 1);
+      return {first, (phys << prm.page_shift) + slot,
+              ((phys * Hkv + kvh) << prm.page_shift) + slot};
+    } else {
+      const int first = min(k0 + kKS * j, k1 - 1);
+      return {first, (long)first, 0};
+    }
   };
-  auto vload = [&](int j, u32x4 (&vx)[NVL]) {
+  // Offset (elements) of key first + i's row from row0's, clamped to the
+  // chunk (first <= k1 - 1 always, so the offset is never negative).
+  auto row_off = [&](const StepRows& st, int i) {
+    return (uint32_t)(min(i, k1 - 1 - st.first) * (int)kstride);
+  };
+  using KX = std::conditional_t<KI8, u32x2, u32x4>;
+  auto kload = [&](const StepRows& st, KX (&kx)[D / 32], f32x4& ksc) {
+    const KE* kr = Kb + st.row0 * kstride + row_off(st, l16);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      if constexpr (KI8) kx[ks] = *reinterpret_cast<const u32x2*>(kr + 32 * ks + 8 * q4);
+      else kx[ks] = load16(kr + 32 * ks + 8 * q4);
+    }
+    // scales of keys first + 4*q4 .. +3 (the score layout below); slots past
+    // the chunk end hold anything and are masked
+    if constexpr (KI8) ksc = *reinterpret_cast<const f32x4*>(prm.ksc + st.srow + 4 * q4);
+  };
+  constexpr int VEPL = VI8 ? 16 : 8;  // elements per 16-byte V load
+  constexpr int VLPR = D / VEPL;      // 16-byte V loads per row
+  auto vload = [&](const StepRows& st, u32x4 (&vx)[NVL], f32x4& vsc) {
+    const VE* vr = Vb + st.row0 * kstride;
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int P = 64 * i + lane;
-      const int key = min(k0 + kKS * j + P / CPR, k1 - 1);
-      vx[i] = load16(Vb + (long)key * kstride + 8 * (P % CPR));
+      vx[i] = *reinterpret_cast<const u32x4*>(vr + row_off(st, P / VLPR) + VEPL * (P % VLPR));
     }
+    if constexpr (VI8) vsc = *reinterpret_cast<const f32x4*>(prm.vsc + st.srow + 4 * q4);
+  };
+  auto load_step = [&](int j, KX (&kx)[D / 32], f32x4& ksc, u32x4 (&vx)[NVL], f32x4& vsc) {
+    const StepRows st = step_rows(j);
+    kload(st, kx, ksc);
+    vload(st, vx, vsc);
   };
   uint16_t* const sv = sV[w];
-  // Row-major V tile [16][D] with 16-byte chunks XOR-swizzled by row.
+  // Row-major V tile [16][D] of 16-bit values with 16-byte chunks
+  // XOR-swizzled by row (int8 codes are widened on the way in).
   auto vstore = [&](const u32x4 (&vx)[NVL]) {
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int P = 64 * i + lane;
-      const int r = P / CPR, c = P % CPR;
-      store16(sv + r * D + 8 * (c ^ swz_dv<D>(r)), vx[i]);
+      const int r = P / VLPR, c = P % VLPR;
+      if constexpr (VI8) {
+        store16(sv + r * D + 8 * ((2 * c) ^ swz_dv<D>(r)), widen8<T>((u32x2){vx[i][0], vx[i][1]}));
+        store16(sv + r * D + 8 * ((2 * c + 1) ^ swz_dv<D>(r)),
+                widen8<T>((u32x2){vx[i][2], vx[i][3]}));
+      } else {
+        store16(sv + r * D + 8 * (c ^ swz_dv<D>(r)), vx[i]);
+      }
     }
   };
   // V^T read for head-dim block db: row 4*q4 + l16/4, columns 16db + 4*(l16%4)
@@ -143,12 +252,17 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
   float m_ref = -INFINITY;
   float l_part = 0.f;
 
-  auto compute = [&](int j, const u32x4 (&kx)[D / 32], const u32x4 (&vx)[NVL]) {
+  auto compute = [&](int j, const KX (&kx)[D / 32], const f32x4& ksc, const u32x4 (&vx)[NVL],
+                     const f32x4& vsc) {
     vstore(vx);  // the previous step's transpose reads of the tile are done (in-order LDS)
     // S^T: keys 4*q4 + r (rows) x heads (columns l16).
     f32x4 s = (f32x4){};
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) s = Ops<T>::mfma16(kx[ks], qf[ks], s);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      if constexpr (KI8) s = Ops<T>::mfma16(widen8<T>(kx[ks]), qf[ks], s);
+      else s = Ops<T>::mfma16(kx[ks], qf[ks], s);
+    }
+    if constexpr (KI8) s *= ksc;  // each key row's scale
     const int lim = k1 - 1 - (k0 + kKS * j) - 4 * q4;  // key offset r visible iff <= lim
     float mx = -INFINITY;
 #pragma unroll
@@ -174,7 +288,15 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const float p2 = exp2_fast(__builtin_fmaf(s[2], scale2, -mb));
     const float p3 = exp2_fast(__builtin_fmaf(s[3], scale2, -mb));
     l_part += (p0 + p1) + (p2 + p3);  // unrounded: lse carries no 16-bit rounding
-    const u32x2 bop = {Ops<T>::pack2(p0, p1), Ops<T>::pack2(p2, p3)};
+    u32x2 bop;
+    if constexpr (VI8) {  // each value row's scale, folded into its probability
+      f32x4 vs = vsc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r > lim) vs[r] = 0.f;  // masked keys: their slot's scale may be anything
+      bop = (u32x2){Ops<T>::pack2(p0 * vs[0], p1 * vs[1]), Ops<T>::pack2(p2 * vs[2], p3 * vs[3])};
+    } else
+      bop = (u32x2){Ops<T>::pack2(p0, p1), Ops<T>::pack2(p2, p3)};
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       acc[db] = Ops<T>::mfma16k16(lds_read_tr16(sv + voff[db]), bop, acc[db]);
@@ -184,21 +306,22 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
   // step computes.  The request is unconditional (past the last step it
   // re-reads the chunk's final row, a cache hit) so that the number of loads
   // in flight, and thus each wait, is the same on every path.
-  u32x4 kA[D / 32], kB[D / 32], vA[NVL], vB[NVL];
-  kload(w, kA);  // (a wave with no step reads the chunk's last row, unused)
-  vload(w, vA);
+  KX kA[D / 32], kB[D / 32];
+  u32x4 vA[NVL], vB[NVL];
+  f32x4 kscA = {}, kscB = {}, vscA = {}, vscB = {};
+  load_step(w, kA, kscA, vA, vscA);  // (a wave with no step reads the chunk's last step, unused)
   // The scheduling barriers keep each request ahead of the wait for the step
-  // being computed, so two steps are in flight while that wait lasts.
+  // being computed, so two steps are in flight while that wait lasts.  (A
+  // third step in flight costs the registers of a second wave per SIMD and
+  // measured slower, for int8 caches too.)
   for (int i = 0; i < my_steps; i += 2) {
-    kload(w + kDW * (i + 1), kB);
-    vload(w + kDW * (i + 1), vB);
+    load_step(w + kDW * (i + 1), kB, kscB, vB, vscB);
     __builtin_amdgcn_sched_barrier(0);
-    compute(w + kDW * i, kA, vA);
+    compute(w + kDW * i, kA, kscA, vA, vscA);
     if (i + 1 >= my_steps) break;
-    kload(w + kDW * (i + 2), kA);
-    vload(w + kDW * (i + 2), vA);
+    load_step(w + kDW * (i + 2), kA, kscA, vA, vscA);
     __builtin_amdgcn_sched_barrier(0);
-    compute(w + kDW * (i + 1), kB, vB);
+    compute(w + kDW * (i + 1), kB, kscB, vB, vscB);
   }
 
   // Merge the waves: full row sums, per-wave normalised output and lse2 to LDS.
@@ -263,33 +386,55 @@ void decode_combine_kernel(const float* __restrict__ Opart, const float* __restr
   if (d == 0) LSE[bh] = (M != -INFINITY) ? (M + __builtin_log2f(tot)) * kLn2 : -INFINITY;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED, bool KI8, bool VI8>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
   const int nhg = (g + 15) / 16;
+  SplitParams p;
+  p.Q = (const uint16_t*)a.q;
+  p.K = a.k;
+  p.V = a.v;
+  p.ksc = a.k_scales;
+  p.vsc = a.v_scales;
+  p.table = a.block_table;
+  p.seqlens = a.seqlens;
+  p.Opart = (float*)a.workspace;
+  p.Lpart = p.Opart + (size_t)a.B * a.Hq * a.num_splits * D;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.Lmax = PAGED ? a.max_pages * a.page_size : a.Lk_max;
+  p.page_shift = PAGED ? __builtin_ctz((unsigned)a.page_size) : 0;
+  p.max_pages = a.max_pages;
+  p.num_pages = a.num_pages;
+  p.S = a.num_splits;
   // |scale| * log2(e), kept >= 1e-30 so masked (-inf) scores give probability 0.
-  const float scale2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
-  const float thr = 8.f / scale2;
-  const uint32_t qxor = (a.scale < 0.f) ? 0x80008000u : 0u;
-  float* Opart = (float*)a.workspace;
-  float* Lpart = Opart + (size_t)a.B * a.Hq * a.num_splits * D;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.num_splits, a.Hkv * nhg, a.B), dim3(64 * kDW), 0,
-                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     a.seqlens, Opart, Lpart, a.Hq, a.Hkv, a.Lk_max, a.num_splits, scale2, thr,
-                     qxor);
+  p.scale2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  p.thr = 8.f / p.scale2;
+  p.qxor = (a.scale < 0.f) ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((decode_split_kernel<T, D, PAGED, KI8, VI8>), dim3(a.num_splits, a.Hkv * nhg, a.B),
+                     dim3(64 * kDW), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, stream,
-                     (const float*)Opart, (const float*)Lpart, (uint16_t*)a.o, a.lse, a.num_splits);
+                     (const float*)p.Opart, (const float*)p.Lpart, (uint16_t*)a.o, a.lse, a.num_splits);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_decode_fmt(const DecodeArgs& a, hipStream_t stream) {
+  if (!a.paged) return launch_decode_t<T, D, false, false, false>(a, stream);
+  if (!a.k_int8 && !a.v_int8) return launch_decode_t<T, D, true, false, false>(a, stream);
+  if (a.k_int8 && !a.v_int8) return launch_decode_t<T, D, true, true, false>(a, stream);
+  if (a.k_int8 && a.v_int8) return launch_decode_t<T, D, true, true, true>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_decode_dtype(const DecodeArgs& a, hipStream_t stream) {
   switch (a.D) {
-    case 64: return launch_decode_t<T, 64>(a, stream);
-    case 128: return launch_decode_t<T, 128>(a, stream);
-    case 256: return launch_decode_t<T, 256>(a, stream);
+    case 64: return launch_decode_fmt<T, 64>(a, stream);
+    case 128: return launch_decode_fmt<T, 128>(a, stream);
+    case 256: return launch_decode_fmt<T, 256>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,6 +36,15 @@ struct DecodeArgs {
   int num_splits;
   void* workspace;
   int bf16;
+  // Paged cache (paged != 0): k/v are [num_pages, page_size, Hkv, D] pages,
+  // block_table [B, max_pages]; page_size a power of two >= 16.
+  int paged = 0;
+  const int* block_table = nullptr;
+  int page_size = 0, max_pages = 0, num_pages = 0;
+  // int8 sides (paged only): codes plus float scales [num_pages, Hkv, page_size].
+  int k_int8 = 0, v_int8 = 0;
+  const float* k_scales = nullptr;
+  const float* v_scales = nullptr;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

@@ -234,6 +234,86 @@ def decode_inputs(cfg: Decode, *, pad_value=float("nan")):
     return q, kc, vc, lens.to(torch.int32)
 
 
+def _kv_side(n, cfg: Decode, g, int8: bool):
+    """n cached rows [n, Hkv, D] of one side: N(0,1) in cfg.dtype, or int8
+    codes round(45 * N(0,1)) clipped to [-127, 127] with float32 scales drawn
+    uniform on [0.018, 0.026] per (row, head) -- about the codes and scales a
+    symmetric per-row int8 quantiser gives for N(0,1) rows of 128 values."""
+    x = torch.randn((n, cfg.Hkv, cfg.D), generator=g, dtype=torch.float32)
+    if not int8:
+        return x.to(cfg.dtype), None
+    codes = torch.round(x * 45.0).clamp(-127, 127).to(torch.int8)
+    scales = torch.rand((n, cfg.Hkv), generator=g, dtype=torch.float32) * 0.008 + 0.018
+    return codes, scales
+
+
+def paged_decode_inputs(cfg: Decode, page_size: int, *, k_int8=False, v_int8=False,
+                        extra_pages=4):
+    """A paged decode cache on the CPU: (q [B,Hq,D], k_pages, v_pages
+    [num_pages, page_size, Hkv, D], k_scales, v_scales (float32
+    [num_pages, Hkv, page_size] or None), block_table int32 [B, max_pages],
+    seqlens int32 [B]).
+
+    Draw order: lengths, Q, a permutation of the physical pages, then for
+    b = 0..B-1 sequence b's K rows then V rows (int8 sides: codes, then
+    scales).  Sequence b's pages are the next ceil(len_b / page_size) pages of
+    the permutation.  Rows no sequence owns -- unused pages, slots past a
+    sequence's end, and the page that table entries past a sequence's end
+    point at -- hold NaN (int8 sides: code 127 with a NaN scale), so any read
+    of them shows in the output.
+    """
+    g = _gen(cfg.seed)
+    lens = torch.randint(cfg.len_lo, cfg.len_hi + 1, (cfg.B,), generator=g, dtype=torch.int64)
+    q = torch.randn((cfg.B, cfg.Hq, cfg.D), generator=g, dtype=torch.float32).to(cfg.dtype)
+    need = [(int(n) + page_size - 1) // page_size for n in lens]
+    max_pages = max(1, (cfg.lmax + page_size - 1) // page_size)
+    num_pages = sum(need) + extra_pages
+    perm = torch.randperm(num_pages, generator=g)
+    junk = int(perm[-1])
+    table = torch.full((cfg.B, max_pages), junk, dtype=torch.int32)
+
+    def pool(int8):
+        if int8:
+            return (torch.full((num_pages, page_size, cfg.Hkv, cfg.D), 127, dtype=torch.int8),
+                    torch.full((num_pages, cfg.Hkv, page_size), float("nan"), dtype=torch.float32))
+        return torch.full((num_pages, page_size, cfg.Hkv, cfg.D), float("nan"), dtype=cfg.dtype), None
+
+    kp, ks = pool(k_int8)
+    vp, vs = pool(v_int8)
+    nxt = 0
+    for b in range(cfg.B):
+        n = int(lens[b])
+        pages = perm[nxt:nxt + need[b]]
+        nxt += need[b]
+        table[b, :need[b]] = pages.to(torch.int32)
+        for pool_x, pool_s, (x, xs) in ((kp, ks, _kv_side(n, cfg, g, k_int8)),
+                                         (vp, vs, _kv_side(n, cfg, g, v_int8))):
+            full, rest = divmod(n, page_size)
+            if full:
+                pool_x[pages[:full]] = x[:full * page_size].reshape(full, page_size, cfg.Hkv, cfg.D)
+                if xs is not None:
+                    pool_s[pages[:full]] = xs[:full * page_size].reshape(
+                        full, page_size, cfg.Hkv).transpose(1, 2)
+            if rest:
+                pool_x[int(pages[full]), :rest] = x[full * page_size:]
+                if xs is not None:
+                    pool_s[int(pages[full]), :, :rest] = xs[full * page_size:].T
+    return q, kp, vp, ks, vs, table, lens.to(torch.int32)
+
+
+def paged_decode_bytes(cfg: Decode, lens, page_size: int, *, k_int8=False, v_int8=False) -> int:
+    """Algorithmic HBM bytes of one paged decode step: every cached row of
+    every sequence read once (2 bytes per element, or 1 plus a 4-byte scale
+    per row for an int8 side), the table entries of the used pages (4 bytes
+    each), q read once, o and lse written once."""
+    lens = [int(x) for x in lens]
+    rows = sum(lens) * cfg.Hkv
+    side = lambda i8: rows * (cfg.D + 4) if i8 else rows * cfg.D * 2
+    entries = sum((n + page_size - 1) // page_size for n in lens)
+    return (side(k_int8) + side(v_int8) + 4 * entries + 2 * cfg.B * cfg.Hq * cfg.D * 2
+            + cfg.B * cfg.Hq * 4)
+
+
 def decode_bytes(cfg: Decode, lens) -> int:
     """Algorithmic HBM bytes of one decode step: the K and V rows of every
     sequence's cache read once, q read once, o and lse written once."""

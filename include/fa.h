@@ -37,6 +37,12 @@ typedef enum {
 
 typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
+/* Storage of one side (keys or values) of a paged KV cache. */
+typedef enum {
+  FA_KV_NATIVE = 0, /* elements of the call's dtype (fp16 / bf16) */
+  FA_KV_INT8 = 1    /* int8 codes; the cached value is code * the row's float scale */
+} fa_kv_format;
+
 /*
  * fa_fwd -- O = softmax(scale * Q K^T + mask) V, computed tile by tile with an
  * online softmax; the score matrix is never stored.
@@ -143,6 +149,48 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
                     void* o, float* lse, int B, int Hq, int Hkv, int Lk_max, int D, float scale,
                     int num_splits, void* workspace, size_t workspace_bytes,
                     fa_dtype dtype, hipStream_t stream);
+
+/*
+ * fa_decode_paged -- fa_decode over a paged KV cache whose keys, or keys and
+ * values, may be stored as int8.
+ *
+ * The cache layout is the PagedAttention one cited in the references of
+ * "FlashAttention-2 (TH)" (systems-analysis.info); the int8 modes are the
+ * KV-INT8 modes of "MNN LLM attention_mode" (lpnh.cn), encoding section
+ * (keys int8 with native values, or both int8).  The pages fix neither the
+ * page layout nor the quantiser; the readings used:
+ *
+ *   k_pages,    device [num_pages, page_size, Hkv, D], elements of `dtype`
+ *   v_pages     (FA_KV_NATIVE) or int8 (FA_KV_INT8); 16-byte aligned.  Key j
+ *               of sequence b is slot j % page_size of page
+ *               block_table[b * max_pages + j / page_size].
+ *   k_scales,   device float32 [num_pages, Hkv, page_size], 16-byte aligned:
+ *   v_scales    the scale of each cached row of an int8 side (its value is
+ *               code * scale); ignored, and may be NULL, for a native side.
+ *               Slots past a sequence's end may hold anything (NaN too).
+ *   block_table device int32 [B, max_pages]; entries are clamped to
+ *               [0, num_pages-1] on the device (bad entries read wrong rows,
+ *               never out of bounds).  Entries past a sequence's length are
+ *               not read.
+ *   seqlens     device int32 [B], clamped to [0, max_pages * page_size].
+ *   page_size   a power of two in [16, 65536].
+ *   k_format,   FA_KV_NATIVE / FA_KV_NATIVE, FA_KV_INT8 / FA_KV_NATIVE or
+ *   v_format    FA_KV_INT8 / FA_KV_INT8 (int8 values with native keys:
+ *               FA_ERR_UNSUPPORTED).
+ *   workspace   as fa_decode: fa_decode_workspace_size(B, Hq, D, num_splits)
+ *               bytes.  Chunks are rounded up to whole 16-key steps here, so
+ *               chunk c covers keys [c*C_b, min(len_b, (c+1)*C_b)) with
+ *               C_b = 16 * ceil(len_b / (16 * num_splits)).
+ *   other arguments as in fa_decode.
+ * Returns FA_OK once both kernels are enqueued.
+ */
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const float* k_scales, const float* v_scales, const int* block_table,
+                          const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv, int D,
+                          int num_pages, int page_size, int max_pages, float scale,
+                          int num_splits, fa_kv_format k_format, fa_kv_format v_format,
+                          void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                          hipStream_t stream);
 
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);

@@ -53,7 +53,8 @@ Sources (page title, section):
 * "MNN LLM attention_mode" (lpnh.cn), encoding section: KV-cache modes with
   the keys, or the keys and the values, stored as int8.  The page gives no
   quantiser; read here as a symmetric int8 code with one float scale per
-  cached row (page, slot, kv head), the cached value being code * scale.
+  cached row (page, slot, kv head), the cached value being code * scale; the
+  scales are laid out [num_pages, Hkv, P].
 
 Implementation notes: each (b, h) pair is independent; rows are processed in
 blocks of ``row_block`` so that at most row_block x Lk scores exist at once.
@@ -238,10 +239,10 @@ def _paged_rows(pages, scales, rows_page, rows_slot, kv):
 
         ip, isl = torch.as_tensor(rows_page), torch.as_tensor(rows_slot)
         x = _as_f64(pages[ip, isl, kv])
-        sc = None if scales is None else _as_f64(scales[ip, isl, kv])
+        sc = None if scales is None else _as_f64(scales[ip, kv, isl])
     else:
         x = _as_f64(np.asarray(pages)[rows_page, rows_slot, kv])
-        sc = None if scales is None else _as_f64(np.asarray(scales)[rows_page, rows_slot, kv])
+        sc = None if scales is None else _as_f64(np.asarray(scales)[rows_page, kv, rows_slot])
     return x if sc is None else x * sc[:, None]
 
 
@@ -252,7 +253,7 @@ def decode_paged_ref(q, k_pages, v_pages, block_table, seqlens, scale: float, *,
     q: [B, Hq, D]; k_pages, v_pages: [num_pages, P, Hkv, D]; block_table:
     [B, max_pages] page numbers; seqlens: [B].  Key j of sequence b is slot
     j % P of page block_table[b, j // P]; sequence b sees keys 0 ..
-    min(seqlens[b], max_pages * P) - 1.  With k_scales ([num_pages, P, Hkv])
+    min(seqlens[b], max_pages * P) - 1.  With k_scales ([num_pages, Hkv, P])
     k_pages holds integer codes and the cached key is code * scale (exact in
     float64); likewise v_scales for the values.  Then the definition of
     ``decode_ref``.  Returns (O [B, Hq, D], lse [B, Hq]) in float64.

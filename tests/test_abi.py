@@ -36,7 +36,8 @@ def lib():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_ex", "fa_decode", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
+        ["fa_fwd", "fa_fwd_ex", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size",
+         "fa_last_error", "fa_info"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -151,3 +152,36 @@ def test_fwd_is_fwd_ex_without_masks(lib):
         e1 = _abi.fa_last_error()
         st2 = fwd_ex(**kw)
         assert (st1, e1) == (st2, _abi.fa_last_error())
+
+
+def dec_paged(**kw):
+    a = dict(q=A16, k=A16, v=A16, ks=None, vs=None, table=A16, seqlens=A16, o=A16, lse=A16, B=2,
+             Hq=8, Hkv=2, D=128, num_pages=10, page_size=16, max_pages=4, scale=0.1,
+             num_splits=8, kf=_abi.FA_KV_NATIVE, vf=_abi.FA_KV_NATIVE, workspace=A16,
+             workspace_bytes=1 << 30, dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_decode_paged(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(table=None), _abi.FA_ERR_INVALID_ARGUMENT, "block_table is NULL"),
+    (dict(seqlens=None), _abi.FA_ERR_INVALID_ARGUMENT, "seqlens is NULL"),
+    (dict(table=A16 + 2), _abi.FA_ERR_INVALID_ARGUMENT, "4-byte aligned"),
+    (dict(page_size=8), _abi.FA_ERR_INVALID_ARGUMENT, "page_size=8"),
+    (dict(page_size=48), _abi.FA_ERR_INVALID_ARGUMENT, "page_size=48"),
+    (dict(page_size=1 << 17), _abi.FA_ERR_INVALID_ARGUMENT, "power of two"),
+    (dict(kf=_abi.FA_KV_INT8), _abi.FA_ERR_INVALID_ARGUMENT, "k_scales"),
+    (dict(kf=_abi.FA_KV_INT8, ks=A16, vf=_abi.FA_KV_INT8), _abi.FA_ERR_INVALID_ARGUMENT,
+     "v_scales"),
+    (dict(vf=_abi.FA_KV_INT8, vs=A16), _abi.FA_ERR_UNSUPPORTED, "int8 values need int8 keys"),
+    (dict(kf=5), _abi.FA_ERR_UNSUPPORTED, "kv formats"),
+    (dict(num_pages=0), _abi.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1"),
+    (dict(max_pages=0), _abi.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1"),
+    (dict(max_pages=1 << 20, page_size=1 << 12), _abi.FA_ERR_INVALID_ARGUMENT, "2^31-1"),
+    (dict(workspace_bytes=64), _abi.FA_ERR_INVALID_ARGUMENT, "needs"),
+    (dict(D=96), _abi.FA_ERR_UNSUPPORTED, "head_dim 96"),
+    (dict(num_splits=65), _abi.FA_ERR_INVALID_ARGUMENT, "num_splits=65"),
+])
+def test_decode_paged_rejects(lib, kw, status, text):
+    assert dec_paged(**kw) == status
+    assert text in _abi.fa_last_error()

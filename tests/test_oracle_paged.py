@@ -26,7 +26,8 @@ def paged_case(seed, B, Hq, Hkv, D, P, lens, *, int8_k=False, int8_v=False, extr
                max_pages=None):
     """A random paged cache: each sequence gets its own pages, in a shuffled
     physical order, plus unused pages filled with large junk.  int8 sides hold
-    integer codes in [-127, 127] with positive per-row scales."""
+    integer codes in [-127, 127] with positive per-row scales
+    ([num_pages, Hkv, P])."""
     r = np.random.default_rng(seed)
     need = [(n + P - 1) // P for n in lens]
     mp = max_pages or max(1, max(need))
@@ -43,7 +44,7 @@ def paged_case(seed, B, Hq, Hkv, D, P, lens, *, int8_k=False, int8_v=False, extr
     def side(is_int8):
         if is_int8:
             codes = r.integers(-127, 128, (num_pages, P, Hkv, D)).astype(np.float64)
-            scales = r.uniform(0.01, 0.05, (num_pages, P, Hkv))
+            scales = r.uniform(0.01, 0.05, (num_pages, Hkv, P))
             return codes, scales
         return r.standard_normal((num_pages, P, Hkv, D)), None
 
@@ -68,8 +69,8 @@ def logical_cache_loops(kp, vp, table, ks, vs, b, n):
         slot = j - (j // P) * P
         for h in range(Hkv):
             for d in range(D):
-                K[0, j, h, d] = kp[page, slot, h, d] * (1.0 if ks is None else ks[page, slot, h])
-                V[0, j, h, d] = vp[page, slot, h, d] * (1.0 if vs is None else vs[page, slot, h])
+                K[0, j, h, d] = kp[page, slot, h, d] * (1.0 if ks is None else ks[page, h, slot])
+                V[0, j, h, d] = vp[page, slot, h, d] * (1.0 if vs is None else vs[page, h, slot])
     return K, V
 
 
@@ -102,8 +103,8 @@ def pin_torch_sdpa(fn):
     lens = [13, 1, 30]
     q, kp, vp, table, ln, ks, vs = paged_case(7, B, Hq, Hkv, D, P, lens, int8_k=True, int8_v=True)
     o, l = fn(q, kp, vp, table, ln, 0.3, k_scales=ks, v_scales=vs)
-    tk = torch.from_numpy(kp * ks[..., None]).reshape(-1, Hkv, D)
-    tv = torch.from_numpy(vp * vs[..., None]).reshape(-1, Hkv, D)
+    tk = torch.from_numpy(kp * ks.transpose(0, 2, 1)[..., None]).reshape(-1, Hkv, D)
+    tv = torch.from_numpy(vp * vs.transpose(0, 2, 1)[..., None]).reshape(-1, Hkv, D)
     for b in range(B):
         rows = torch.tensor([int(table[b][j // P]) * P + j % P for j in range(lens[b])])
         K = tk.index_select(0, rows).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
