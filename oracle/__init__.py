@@ -21,6 +21,9 @@ Contents
 ``attention.decode_paged_ref``
     Decode against a paged KV cache (page table per sequence), optionally
     with int8 keys and/or values carrying one scale per cached row.
+``backward.attention_bwd_ref``
+    The gradients of the definition with respect to Q, K and V given dO
+    (the chain rule through scores, row softmax and weighted sum), float64.
 ``online.online_attention_ref`` / ``online.split_combine_ref``
     The blockwise online-softmax recurrence and the logsumexp merge of
     key-chunk summaries, restated in float64 from the pages.  These are
@@ -34,10 +37,12 @@ than itself: a 40-digit ``decimal`` brute force, PyTorch's fp64 CPU
 
 from .attention import (attention_ref, causal_allowed, decode_paged_ref, decode_ref, key_bounds,
                         varlen_ref)
+from .backward import attention_bwd_ref
 from .online import online_attention_ref, split_combine_ref
 
 __all__ = [
     "attention_ref",
+    "attention_bwd_ref",
     "decode_ref",
     "decode_paged_ref",
     "causal_allowed",

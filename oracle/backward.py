@@ -1,0 +1,131 @@
+"""Gradients of the attention definition, in float64 -- the oracle's backward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+What is computed
+----------------
+The forward (``attention.py``) maps Q, K, V to O with, for one (batch, query
+head), scores s_ij = scale * q_i . k_j, the allowed key sets A_i (causal /
+window rules), P_ij = softmax over A_i of s_i. (0 off A_i) and O_i =
+sum_j P_ij v_j.  The backward takes the gradient dO of some loss with respect
+to O and returns the gradients with respect to Q, K and V -- the chain rule
+through those three lines, written out:
+
+  dv_j   = sum_i P_ij dO_i
+  dP_ij  = dO_i . v_j
+  D_i    = sum_j P_ij dP_ij            (equals dO_i . O_i)
+  dS_ij  = P_ij (dP_ij - D_i)          (the softmax Jacobian applied to dP)
+  dq_i   = scale * sum_j dS_ij k_j
+  dk_j   = scale * sum_i dS_ij q_i
+
+With grouped K/V heads (query head h reads K/V head h // (Hq / Hkv)) dK and
+dV of a K/V head sum the contributions of every query head of its group.
+Rows with no allowed key have P = 0 and contribute nothing.
+
+Sources (page title, section): the pages define only the forward; "FlashAttention-
+2 (TH)" (systems-analysis.info), performance, reports forward-plus-backward
+training throughput, and "5 years, 10K stars: xformers" (cloud.tencent.com)
+pairs each forward operator with a backward one.  The gradient of the forward
+definition is fixed by calculus; it is pinned in tests by finite differences
+of the forward oracle and by PyTorch autograd.
+
+Implementation notes: one (batch, K/V head) at a time, its query heads in
+turn, query rows in blocks of ``row_block``; P is recomputed from the
+definition (the kernel's saved lse is not an input here).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _as_f64, row_bounds
+
+
+def _head_backward(qh, kh, vh, doh, scale, causal, window, row_block, bounds):
+    """One (batch, query head): qh, doh [Lq, D]; kh, vh [Lk, D].  Returns
+    dq [Lq, D], dk [Lk, D], dv [Lk, Dv] and, with ``bounds``, the sums of the
+    absolute values of the terms of each of them (same shapes)."""
+    Lq, D = qh.shape
+    Lk = kh.shape[0]
+    dq = np.zeros_like(qh)
+    dk = np.zeros_like(kh)
+    dv = np.zeros((Lk, vh.shape[1]))
+    abs_q = np.zeros_like(qh) if bounds else None
+    abs_k = np.zeros_like(kh) if bounds else None
+    abs_v = np.zeros((Lk, vh.shape[1])) if bounds else None
+    if Lk == 0:
+        return dq, dk, dv, abs_q, abs_k, abs_v
+    cols = np.arange(Lk)[None, :]
+    for r0 in range(0, Lq, row_block):
+        r1 = min(Lq, r0 + row_block)
+        lo, hi = row_bounds(np.arange(r0, r1), Lq, Lk, causal, window)
+        allowed = (cols >= lo[:, None]) & (cols <= hi[:, None])
+        s = np.where(allowed, scale * (qh[r0:r1] @ kh.T), -np.inf)
+        m = s.max(axis=1)
+        m_safe = np.where(np.isfinite(m), m, 0.0)
+        e = np.exp(s - m_safe[:, None])
+        l = e.sum(axis=1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            p = np.where(l[:, None] > 0, e / l[:, None], 0.0)        # P, 0 off A_i
+        do = doh[r0:r1]
+        dv += p.T @ do
+        dp = do @ vh.T
+        d_i = (p * dp).sum(axis=1)
+        ds = p * (dp - d_i[:, None])
+        dq[r0:r1] = scale * (ds @ kh)
+        dk += scale * (ds.T @ qh[r0:r1])
+        if bounds:
+            abs_v += p.T @ np.abs(do)
+            ads = np.abs(ds)
+            abs_q[r0:r1] = abs(scale) * (ads @ np.abs(kh))
+            abs_k += abs(scale) * (ads.T @ np.abs(qh[r0:r1]))
+    return dq, dk, dv, abs_q, abs_k, abs_v
+
+
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, *, window=(-1, -1),
+                      kv_heads=None, row_block: int = 512, bounds: bool = False):
+    """Gradients of ``attention_ref``'s O with respect to q, k, v, given dO.
+
+    q, do: [B, Lq, Hq, D]; k, v: [B, Lk, Hkv, D].  Returns (dq, dk, dv) in
+    float64 with the shapes of q, k, v; with ``bounds`` also (abs_dq, abs_dk,
+    abs_dv), the per-element sums of |terms| of each gradient (for error
+    bounds).  ``kv_heads`` optionally restricts the work to a list of
+    (b, kv head) pairs: their dK, dV and the dQ of their query heads are
+    computed, everything else is NaN.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if Hkv < 1 or Hq % Hkv or do.shape != q.shape:
+        raise ValueError("shape mismatch")
+    g = Hq // Hkv
+    scale = float(scale)
+    out = [np.full(q.shape, np.nan), np.full(k.shape, np.nan), np.full(v.shape, np.nan)]
+    absd = [np.full(x.shape, np.nan) for x in out] if bounds else None
+    jobs = list(kv_heads) if kv_heads is not None else [(b, c) for b in range(B)
+                                                          for c in range(Hkv)]
+    for b, c in jobs:
+        dk_acc = np.zeros((Lk, D))
+        dv_acc = np.zeros((Lk, v.shape[3]))
+        ak_acc = np.zeros((Lk, D))
+        av_acc = np.zeros((Lk, v.shape[3]))
+        for h in range(c * g, (c + 1) * g):
+            dq, dk, dv, aq, ak, av = _head_backward(q[b, :, h], k[b, :, c], v[b, :, c],
+                                                    do[b, :, h], scale, causal, tuple(window),
+                                                    row_block, bounds)
+            out[0][b, :, h] = dq
+            dk_acc += dk
+            dv_acc += dv
+            if bounds:
+                absd[0][b, :, h] = aq
+                ak_acc += ak
+                av_acc += av
+        out[1][b, :, c] = dk_acc
+        out[2][b, :, c] = dv_acc
+        if bounds:
+            absd[1][b, :, c] = ak_acc
+            absd[2][b, :, c] = av_acc
+    if bounds:
+        return tuple(out) + tuple(absd)
+    return tuple(out)
