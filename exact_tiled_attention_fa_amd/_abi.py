@@ -42,6 +42,9 @@ SIGNATURES = {
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                              _I, _I, _I, _P, _Z, _I, _P]),
+    "fa_bwd_workspace_size": (_Z, [_I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P,
+                    _Z, _I, _P]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_info": (ctypes.c_char_p, []),
 }
@@ -104,6 +107,16 @@ def fa_decode_paged(q, k_pages, v_pages, k_scales, v_scales, block_table, seqlen
                                   lse, B, Hq, Hkv, D, num_pages, page_size, max_pages, scale,
                                   num_splits, k_format, v_format, workspace, workspace_bytes,
                                   dtype, stream)
+
+
+def fa_bwd_workspace_size(B, Hq, Lq) -> int:
+    return load().fa_bwd_workspace_size(B, Hq, Lq)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, window_left,
+           window_right, workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
+                         window_left, window_right, workspace, workspace_bytes, dtype, stream)
 
 
 def fa_last_error() -> str:

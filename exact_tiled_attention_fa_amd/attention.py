@@ -83,6 +83,42 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, softmax
     return out, lse
 
 
+def flash_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                   lse: torch.Tensor, dout: torch.Tensor, *, softmax_scale=None,
+                   causal: bool = False, window=(-1, -1), dq=None, dk=None, dv=None,
+                   workspace=None):
+    """Gradients of flash_attn_fwd: returns (dq [B,Lq,Hq,D], dk, dv [B,Lk,Hkv,D])
+    in q's dtype from the forward's inputs, its output ``out`` and ``lse``,
+    and the output gradient ``dout``.  D in {64, 128}."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse"), (dout, "dout")):
+        _check_dev(t, n)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or out.shape != q.shape:
+        raise ValueError("expected q, out [B,Lq,Hq,D] and k, v [B,Lk,Hkv,D]")
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout must share dtype float16 or bfloat16")
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, Lq):
+        raise ValueError("lse must be float32 [B, Hq, Lq]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        n = _abi.fa_bwd_workspace_size(B, Hq, Lq)
+        workspace = torch.empty((max(n, 16),), dtype=torch.uint8, device=q.device)
+    st = _abi.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Lq,
+                     Lk, D, scale, 1 if causal else 0, int(window[0]), int(window[1]),
+                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                     _DTYPES[q.dtype], _stream_handle(q.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv
+
+
 def flash_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                       cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
                       softmax_scale=None, causal: bool = False, window=(-1, -1), out=None,

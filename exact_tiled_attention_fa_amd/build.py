@@ -25,7 +25,7 @@ OUT_DIR = PKG / "_lib"
 LIB = OUT_DIR / "libfa.so"
 OBJ_DIR = ROOT / "_build"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -233,6 +233,59 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
   return ok();
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Lq) {
+  if (B < 1 || Hq < 1 || Lq < 1) return 0;
+  return fa::bwd_workspace_bytes(B, Hq, Lq);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq,
+                 int Lk, int D, float scale, int causal, int window_left, int window_right,
+                 void* workspace, size_t workspace_bytes, fa_dtype dtype, hipStream_t stream) {
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k, "k"));
+  FA_TRY(check_ptr(v, "v"));
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(dout, "dout"));
+  FA_TRY(check_ptr(lse, "lse"));
+  FA_TRY(check_ptr(dq, "dq"));
+  FA_TRY(check_ptr(dk, "dk"));
+  FA_TRY(check_ptr(dv, "dv"));
+  FA_TRY(check_ptr(workspace, "workspace"));
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || D < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d)", B, Hq, Hkv, Lq, Lk, D);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)dtype);
+  if (D != 64 && D != 128)
+    return fail(FA_ERR_UNSUPPORTED, "backward head_dim %d not in {64, 128}", D);
+  if ((long long)Hq * D >= (1LL << 25) || (long long)Hkv * D >= (1LL << 25))
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hq * D and Hkv * D must be < 2^25");
+  if ((long long)B * Lq * Hq > 0x7fffffffLL || (long long)B * Lk * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
+  if (B > 65535 || Hq > 65535)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (B or Hq exceeds 65535)");
+  const long long span = (long long)B * Lq + (long long)B * Lk;
+  const bool windowed = window_left >= 0 || window_right >= 0;
+  if (windowed && span > (1LL << 30))
+    return fail(FA_ERR_INVALID_ARGUMENT, "windowed attention needs query + key rows <= 2^30");
+  const size_t need = fa::bwd_workspace_bytes(B, Hq, Lq);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                need);
+
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal ? 1 : 0,
+                (window_left < 0 || window_left >= span) ? -1 : window_left,
+                (window_right < 0 || window_right >= span) ? -1 : window_right, workspace,
+                dtype == FA_BF16 ? 1 : 0};
+  hipError_t e = fa::launch_bwd(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* fa_last_error(void) { return g_err; }
 
 const char* fa_info(void) {

@@ -1,0 +1,549 @@
+// Backward pass: dQ, dK, dV of exact attention from Q, K, V, O, dO and the
+// forward's per-row logsumexp.
+//
+// The gradients are those of the forward's definition (row softmax of the
+// scaled scores, weighted sum of values).  Training with the method is
+// reported in "FlashAttention-2 (TH)" (systems-analysis.info), performance,
+// and "5 years, 10K stars: xformers" (cloud.tencent.com) pairs each attention
+// forward with a backward; neither page spells the backward out.  Written
+// per (query i, key j) of one head, with P_ij = exp(s_ij - lse_i) rebuilt
+// from the saved lse (no N x N buffer, as in the forward):
+//   dV_j += P_ij dO_i          dP_ij = dO_i . V_j         D_i = dO_i . O_i
+//   dS_ij = P_ij (dP_ij - D_i)  dQ_i += scale dS_ij K_j   dK_j += scale dS_ij Q_i
+//
+// Three kernels, none of them with atomics (results are bitwise
+// reproducible):
+//   * prep: D_i and lse_i * log2(e) per row into a workspace (+inf for rows
+//     that see no key, so their probabilities come out 0).
+//   * dq (query-major, like the forward): a workgroup owns 128 query rows (32
+//     per wave, one per lane column) and streams K/V tiles of 32 keys through
+//     LDS (LDS-direct copies, two stages).  Per tile and wave:
+//     S^T = K Q^T and dP^T = V dO^T with v_mfma_f32_32x32x16 (A = K or V rows
+//     from LDS, B = Q^T or dO^T held in registers), then dS^T in registers,
+//     then dQ^T += K^T dS^T (A = K^T by transpose reads of the same K tile,
+//     B = dS^T straight from the accumulator, rounded to 16 bits).
+//   * dkdv (key-major): a workgroup owns 128 keys (32 per wave, one per lane
+//     column) of one K/V head and streams tiles of 32 query rows of every
+//     query head of its group (Q, dO, lse, D) through LDS.  Per tile and wave:
+//     S = Q K^T and dP = dO V^T (A = Q or dO rows from LDS, B = K^T or V^T in
+//     registers), then P and dS, then dV^T += dO^T P and dK^T += Q^T dS (A by
+//     transpose reads of the dO and Q tiles).  The group's query heads add
+//     into the same accumulators, so GQA needs no reduction pass.
+// Masks (causal, sliding window, the key count) are those of the forward;
+// tiles a wave's rows cannot see are skipped, partly visible ones are masked.
+#include <type_traits>
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kBW = 4;         // waves per workgroup
+constexpr int kBT = kBW * 64;  // threads per workgroup
+constexpr int kBR = 32;        // rows per wave (queries in dq, keys in dkdv)
+constexpr int kBM = kBW * kBR; // rows per workgroup
+constexpr int kTile = 32;      // rows per streamed tile (keys in dq, queries in dkdv)
+
+struct BwdParams {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* O;
+  const uint16_t* dO;
+  const float* LSE;
+  uint16_t* dQ;
+  uint16_t* dK;
+  uint16_t* dV;
+  float* lse2;  // workspace [B, Hq, Lqp]: lse * log2(e), +inf for rows with no key
+  float* Dd;    // workspace [B, Hq, Lqp]: rowsum(dO * O)
+  int B, Hq, Hkv, Lq, Lk, Lqp;
+  int win_left, win_right;
+  float scale2;  // |scale| * log2(e), >= 1e-30
+  float scale;   // signed scale (factor of dQ and dK)
+  uint32_t qxor; // sign flip of q for negative scales
+};
+
+// XOR on a row's 16-byte chunk index in the LDS tiles (row reads of 16
+// consecutive rows at one logical chunk hit distinct banks).
+template <int D> __device__ __forceinline__ int swz_b(int r) {
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Per-row statistics: D_i = dO_i . O_i and lse_i * log2(e).  CPR lanes (one
+// 16-byte chunk each) per (row, head); rows in memory order [B, Lq, Hq].
+template <typename T, int D>
+__global__ __launch_bounds__(256)
+void bwd_prep_kernel(const BwdParams p) {
+  constexpr int CPR = D / 8;
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = gid / CPR;  // (b * Lq + i) * Hq + h
+  const int c = (int)(gid % CPR);
+  const long nrows = (long)p.B * p.Lq * p.Hq;
+  float acc = 0.f;
+  const bool valid = row < nrows;
+  if (valid) {
+    const u32x4 o = load16(p.O + row * D + 8 * c);
+    const u32x4 g = load16(p.dO + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc += Ops<T>::lo(o[e]) * Ops<T>::lo(g[e]) + Ops<T>::hi(o[e]) * Ops<T>::hi(g[e]);
+  }
+#pragma unroll
+  for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (valid && c == 0) {
+    const int h = (int)(row % p.Hq);
+    const long bi = row / p.Hq;
+    const int i = (int)(bi % p.Lq);
+    const int b = (int)(bi / p.Lq);
+    const long oi = ((long)b * p.Hq + h) * p.Lqp + i;
+    const float l = p.LSE[((long)b * p.Hq + h) * p.Lq + i];
+    p.Dd[oi] = acc;
+    p.lse2[oi] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// LDS-direct copy of `rows` x D 16-bit elements (rows r0 .. r0+rows-1 of a
+// matrix with row stride `stride` elements; rows past `last` re-read `last`)
+// into an LDS tile, 16-byte chunks XOR-swizzled by row.  Every thread of the
+// workgroup takes part.
+template <int D, int ROWS>
+struct TileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int NLOAD = ROWS * CPR / kBT;
+  static_assert((ROWS * CPR) % kBT == 0, "tile shape");
+  uint32_t off[NLOAD];
+  int rr[NLOAD];
+  __device__ __forceinline__ void init(int wu, int lane, int stride) {
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      const int P = (i * kBW + wu) * 64 + lane;
+      const int r = P / CPR, pc = P % CPR;
+      rr[i] = r;
+      off[i] = 2u * (uint32_t)(r * stride + 8 * (pc ^ swz_b<D>(r)));
+    }
+  }
+  __device__ __forceinline__ void issue(const uint16_t* src, int r0, int last, int stride, int wu,
+                                        uint16_t* dst) const {
+    const uint16_t* base = src + (long)r0 * stride;
+    const bool whole = r0 + ROWS - 1 <= last;
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      uint32_t o = off[i];
+      if (!whole) o -= 2u * (uint32_t)(((r0 + rr[i]) - min(r0 + rr[i], last)) * stride);
+      load_lds16_off(base, o, dst + (i * kBW + wu) * 512);
+    }
+  }
+};
+
+// Wait for this wave's copies, then the workgroup barrier (no __syncthreads:
+// its fence would also order the LDS-direct copies issued after it).
+__device__ __forceinline__ void copies_done_barrier() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~0x0F00);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int D>
+__device__ __forceinline__ u32x4 ld_row_chunk(const uint16_t* tile, int r, int chunk) {
+  return *reinterpret_cast<const u32x4*>(tile + r * D + 8 * (chunk ^ swz_b<D>(r)));
+}
+
+// Transpose-read offsets: lane (16-lane group position i) of half hf reads
+// row 4*hf + (i/4) (+8 for the second half of a 16-row step), columns
+// 32*db + 16*((lane/16)%2) + 4*(lane%4) .. +3; after ds_read_b64_tr_b16 the
+// lane holds one column of four consecutive rows: the A operand of an MFMA
+// whose B operand is the 32x32 accumulator layout.
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&toff)[D / 32][2]) {
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 8 * half + 4 * hf + ((lane & 15) >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      toff[db][half] = row * D + 8 * ((col >> 3) ^ swz_b<D>(row)) + (col & 7);
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ f32x16 mfma_tr(const uint16_t* tile, const int (&toff)[D / 32][2],
+                                           int db, int ts, u32x4 bop, f32x16 acc) {
+  const u32x2 lo = lds_read_tr16(tile + 16 * ts * D + toff[db][0]);
+  const u32x2 hi = lds_read_tr16(tile + 16 * ts * D + toff[db][1]);
+  return Ops<T>::mfma32((u32x4){lo[0], lo[1], hi[0], hi[1]}, bop, acc);
+}
+
+// -------------------------------------------------------------------------
+// dQ: query-major.
+// -------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBT, 2)
+void bwd_dq_kernel(const BwdParams p) {
+  constexpr int BN = kTile;
+  constexpr int TILE = BN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+
+  const int Hq = p.Hq, Lq = p.Lq, Lk = p.Lk;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int nqt = (Lq + kBM - 1) / kBM;
+  const int qt = CAUSAL ? nqt - 1 - (int)blockIdx.x : (int)blockIdx.x;  // heaviest first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / (Hq / p.Hkv);
+  const int shift = Lk - Lq;
+  const int q0 = qt * kBM, qw0 = q0 + kBR * w, qrow = qw0 + l32;
+  const int wl = p.win_left, wr = p.win_right;
+  auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
+  auto kmax = [&](int i) {
+    int hi = Lk - 1;
+    if (CAUSAL) hi = min(hi, i + shift);
+    if (wr >= 0) hi = min(hi, i + shift + wr);
+    return hi;
+  };
+  const long qstride = (long)Hq * D;
+  const int kstride = p.Hkv * D;
+  const uint16_t* Kb = p.K + (long)b * Lk * kstride + (long)kvh * D;
+  const uint16_t* Vb = p.V + (long)b * Lk * kstride + (long)kvh * D;
+
+  // Q^T and dO^T operands: lane holds query qrow, 8 dims per 16-dim k-step.
+  u32x4 qf[D / 16], df[D / 16];
+  const long rowbase = ((long)b * Lq + min(qrow, Lq - 1)) * qstride + (long)h * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = load16(p.Q + rowbase + 16 * s + 8 * hf) ^ p.qxor;
+    df[s] = load16(p.dO + rowbase + 16 * s + 8 * hf);
+  }
+  const long si = ((long)b * Hq + h) * p.Lqp + qrow;
+  const float lse2 = qrow < Lq ? p.lse2[si] : INFINITY;
+  const float Dq = qrow < Lq ? p.Dd[si] : 0.f;
+  const float scale2 = p.scale2;
+
+  const int q_last = min(q0 + kBM, Lq) - 1;
+  const int wg_lo = kmin(q0), wg_hi = kmax(q_last);
+  const int t_first = wg_lo / BN;
+  const int ntiles = wg_hi >= wg_lo ? wg_hi / BN - t_first + 1 : 0;
+  const int qw_last = min(qw0 + kBR - 1, Lq - 1);
+  const bool wave_live = qw0 < Lq && kmax(qw_last) >= kmin(qw0);
+  const int first_live = wave_live ? kmin(qw0) / BN - t_first : ntiles;
+  const int last_live = wave_live ? kmax(qw_last) / BN - t_first : -1;
+  const int row_kmin = kmin(qrow), row_kmax = kmax(qrow);
+
+  TileLoader<D, BN> ldr;
+  ldr.init(wu, lane, kstride);
+  int toff[D / 32][2];
+  tr_offsets<D>(lane, toff);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+
+  auto compute = [&](int u, const uint16_t* sK, const uint16_t* sV) {
+    const int j0 = (t_first + u) * BN;
+    f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = Ops<T>::mfma32(ld_row_chunk<D>(sK, l32, 2 * kk + hf), qf[kk], s);
+      dp = Ops<T>::mfma32(ld_row_chunk<D>(sV, l32, 2 * kk + hf), df[kk], dp);
+    }
+    // key j0 + 8(r/4) + 4hf + r%4 of query qrow: visible iff in [row_kmin, row_kmax]
+    const bool whole = j0 >= kmin(qw_last) && j0 + BN - 1 <= kmax(qw0) && qw0 + kBR <= Lq;
+    const int lo = row_kmin - j0 - 4 * hf, hi = row_kmax - j0 - 4 * hf;
+    uint32_t dsk[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      float d2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * jj + e;
+        const int off = 8 * (r >> 2) + (r & 3);
+        const float pr = exp2_fast(__builtin_fmaf(s[r], scale2, -lse2));
+        const float ds = pr * (dp[r] - Dq);
+        d2[e] = (whole || (off >= lo && off <= hi)) ? ds : 0.f;
+      }
+      dsk[jj] = Ops<T>::pack2(d2[0], d2[1]);
+    }
+    // dQ^T += K^T dS^T, 16 keys per k-step
+#pragma unroll
+    for (int ts = 0; ts < BN / 16; ++ts) {
+      const u32x4 bop = {dsk[4 * ts], dsk[4 * ts + 1], dsk[4 * ts + 2], dsk[4 * ts + 3]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma_tr<T, D>(sK, toff, db, ts, bop, acc[db]);
+    }
+  };
+
+  if (ntiles > 0) {
+    ldr.issue(Kb, t_first * BN, Lk - 1, kstride, wu, sK0);
+    ldr.issue(Vb, t_first * BN, Lk - 1, kstride, wu, sV0);
+    for (int u = 0; u < ntiles; u += 2) {
+      copies_done_barrier();
+      if (u + 1 < ntiles) {
+        ldr.issue(Kb, (t_first + u + 1) * BN, Lk - 1, kstride, wu, sK1);
+        ldr.issue(Vb, (t_first + u + 1) * BN, Lk - 1, kstride, wu, sV1);
+      }
+      if (u >= first_live && u <= last_live) compute(u, sK0, sV0);
+      if (u + 1 >= ntiles) break;
+      copies_done_barrier();
+      if (u + 2 < ntiles) {
+        ldr.issue(Kb, (t_first + u + 2) * BN, Lk - 1, kstride, wu, sK0);
+        ldr.issue(Vb, (t_first + u + 2) * BN, Lk - 1, kstride, wu, sV0);
+      }
+      if (u + 1 >= first_live && u + 1 <= last_live) compute(u + 1, sK1, sV1);
+    }
+  }
+
+  if (qrow < Lq) {
+    uint16_t* out = p.dQ + ((long)b * Lq + qrow) * qstride + (long)h * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 val = {Ops<T>::pack2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
+                           Ops<T>::pack2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
+        *reinterpret_cast<u32x2*>(out + 32 * db + 8 * g + 4 * hf) = val;
+      }
+  }
+}
+
+// -------------------------------------------------------------------------
+// dK, dV: key-major.
+// -------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBT, 1)
+void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int BQ = kTile;
+  constexpr int TILE = BQ * D;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG1[TILE];
+  __shared__ __attribute__((aligned(16))) float sL0[2 * BQ];  // lse2 then D of the tile's rows
+  __shared__ __attribute__((aligned(16))) float sL1[2 * BQ];
+
+  const int Hq = p.Hq, Hkv = p.Hkv, Lq = p.Lq, Lk = p.Lk;
+  const int g = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int kt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;  // kt ascending: heaviest first
+  const int shift = Lk - Lq;
+  const int k0 = kt * kBM, kw0 = k0 + kBR * w, key = kw0 + l32;
+  const int k_last = min(k0 + kBM, Lk) - 1;
+  const int kw_last = min(kw0 + kBR - 1, Lk - 1);
+  const int wl = p.win_left, wr = p.win_right;
+  auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
+  auto kmax = [&](int i) {
+    int hi = Lk - 1;
+    if (CAUSAL) hi = min(hi, i + shift);
+    if (wr >= 0) hi = min(hi, i + shift + wr);
+    return hi;
+  };
+  // Query rows that can see some key in [ka, kb]: [qlo(ka), qhi(kb)].
+  auto qlo = [&](int ka) {
+    int lo = 0;
+    if (CAUSAL) lo = max(lo, ka - shift);
+    if (wr >= 0) lo = max(lo, ka - shift - wr);
+    return lo;
+  };
+  auto qhi = [&](int kb) { return wl < 0 ? Lq - 1 : min(Lq - 1, kb - shift + wl); };
+
+  const int kstride = Hkv * D;
+  const int qstride = Hq * D;
+  // K^T and V^T operands: lane holds key `key` (clamped), 8 dims per k-step.
+  u32x4 kf[D / 16], vf[D / 16];
+  const long krow = ((long)b * Lk + min(key, Lk - 1)) * kstride + (long)kvh * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kf[s] = load16(p.K + krow + 16 * s + 8 * hf);
+    vf[s] = load16(p.V + krow + 16 * s + 8 * hf);
+  }
+
+  const int i_lo = qlo(k0), i_hi = qhi(k_last);
+  const int s_first = i_lo / BQ;
+  const int nsteps = (k0 < Lk && i_hi >= i_lo) ? i_hi / BQ - s_first + 1 : 0;
+  const int wi_lo = qlo(kw0), wi_hi = qhi(kw_last);
+  const bool wave_live = kw0 < Lk && wi_hi >= wi_lo;
+  const int first_live = wave_live ? wi_lo / BQ - s_first : nsteps;
+  const int last_live = wave_live ? wi_hi / BQ - s_first : -1;
+  const int ntiles = g * nsteps;  // (query head of the group, query step) pairs
+
+  TileLoader<D, BQ> ldr;
+  ldr.init(wu, lane, qstride);
+  int toff[D / 32][2];
+  tr_offsets<D>(lane, toff);
+
+  // lse2 / D copy: wave 0, lanes 0..15 (8 chunks of 4 rows each).
+  auto issue_tile = [&](int u, uint16_t* dq_tile, uint16_t* dg_tile, float* dl) {
+    const int hh = kvh * g + u / nsteps;
+    const int q0 = (s_first + u % nsteps) * BQ;
+    const long hbase = (long)b * Lq * qstride + (long)hh * D;
+    ldr.issue(p.Q + hbase, q0, Lq - 1, qstride, wu, dq_tile);
+    ldr.issue(p.dO + hbase, q0, Lq - 1, qstride, wu, dg_tile);
+    if (wu == 0 && lane < 16) {
+      const long sb = ((long)b * Hq + hh) * p.Lqp + q0;  // rows q0..q0+31 < Lqp
+      const float* src = (lane < 8 ? p.lse2 : p.Dd) + sb + 4 * (lane & 7);
+      load_lds16(src, dl);
+    }
+  };
+
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dv[i] = (f32x16){};
+    dk[i] = (f32x16){};
+  }
+  const float scale2 = p.scale2;
+  const uint32_t qxor = p.qxor;
+
+  auto compute = [&](int u, const uint16_t* sQ, const uint16_t* sG, const float* sL) {
+    const int st = u % nsteps;
+    if (st < first_live || st > last_live) return;
+    const int q0 = (s_first + st) * BQ;
+    f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = Ops<T>::mfma32(ld_row_chunk<D>(sQ, l32, 2 * kk + hf) ^ qxor, kf[kk], s);
+      dp = Ops<T>::mfma32(ld_row_chunk<D>(sG, l32, 2 * kk + hf), vf[kk], dp);
+    }
+    // element r: query q0 + 8(r/4) + 4hf + r%4, key `key`
+    const int qlast = min(q0 + BQ, Lq) - 1;
+    const bool whole = q0 + BQ <= Lq && kw0 >= kmin(qlast) && kw0 + kBR - 1 <= kmax(q0) &&
+                       kw0 + kBR <= Lk;
+    uint32_t pk[8], dsk[8];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 8 * gq + 4 * hf);
+      const f32x4 D4 = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * gq + 4 * hf);
+      float pr[4], ds[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * gq + i;
+        const int qi = q0 + 8 * gq + 4 * hf + i;
+        const bool vis = whole || (qi < Lq && key >= kmin(qi) && key <= kmax(qi));
+        const float e = exp2_fast(__builtin_fmaf(s[r], scale2, -L4[i]));
+        pr[i] = vis ? e : 0.f;
+        ds[i] = vis ? e * (dp[r] - D4[i]) : 0.f;
+      }
+      pk[2 * gq] = Ops<T>::pack2(pr[0], pr[1]);
+      pk[2 * gq + 1] = Ops<T>::pack2(pr[2], pr[3]);
+      dsk[2 * gq] = Ops<T>::pack2(ds[0], ds[1]);
+      dsk[2 * gq + 1] = Ops<T>::pack2(ds[2], ds[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per k-step
+#pragma unroll
+    for (int ts = 0; ts < BQ / 16; ++ts) {
+      const u32x4 pb = {pk[4 * ts], pk[4 * ts + 1], pk[4 * ts + 2], pk[4 * ts + 3]};
+      const u32x4 db_ = {dsk[4 * ts], dsk[4 * ts + 1], dsk[4 * ts + 2], dsk[4 * ts + 3]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dv[db] = mfma_tr<T, D>(sG, toff, db, ts, pb, dv[db]);
+        dk[db] = mfma_tr<T, D>(sQ, toff, db, ts, db_, dk[db]);
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    issue_tile(0, sQ0, sG0, sL0);
+    for (int u = 0; u < ntiles; u += 2) {
+      copies_done_barrier();
+      if (u + 1 < ntiles) issue_tile(u + 1, sQ1, sG1, sL1);
+      compute(u, sQ0, sG0, sL0);
+      if (u + 1 >= ntiles) break;
+      copies_done_barrier();
+      if (u + 2 < ntiles) issue_tile(u + 2, sQ0, sG0, sL0);
+      compute(u + 1, sQ1, sG1, sL1);
+    }
+  }
+
+  if (key < Lk) {
+    const long orow = ((long)b * Lk + key) * kstride + (long)kvh * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int d = 32 * db + 8 * gg + 4 * hf;
+        *reinterpret_cast<u32x2*>(p.dK + orow + d) =
+            (u32x2){Ops<T>::pack2(dk[db][4 * gg] * sc, dk[db][4 * gg + 1] * sc),
+                    Ops<T>::pack2(dk[db][4 * gg + 2] * sc, dk[db][4 * gg + 3] * sc)};
+        *reinterpret_cast<u32x2*>(p.dV + orow + d) =
+            (u32x2){Ops<T>::pack2(dv[db][4 * gg], dv[db][4 * gg + 1]),
+                    Ops<T>::pack2(dv[db][4 * gg + 2], dv[db][4 * gg + 3])};
+      }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.Q = (const uint16_t*)a.q;
+  p.K = (const uint16_t*)a.k;
+  p.V = (const uint16_t*)a.v;
+  p.O = (const uint16_t*)a.o;
+  p.dO = (const uint16_t*)a.dout;
+  p.LSE = a.lse;
+  p.dQ = (uint16_t*)a.dq;
+  p.dK = (uint16_t*)a.dk;
+  p.dV = (uint16_t*)a.dv;
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.Lq = a.Lq;
+  p.Lk = a.Lk;
+  p.Lqp = bwd_padded_rows(a.Lq);
+  p.lse2 = (float*)a.workspace;
+  p.Dd = p.lse2 + (size_t)a.B * a.Hq * p.Lqp;
+  p.win_left = a.win_left;
+  p.win_right = a.win_right;
+  p.scale2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  p.scale = a.scale;
+  p.qxor = a.scale < 0.f ? 0x80008000u : 0u;
+
+  const long nrows = (long)a.B * a.Lq * a.Hq;
+  const long nthreads = nrows * (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 gq((a.Lq + kBM - 1) / kBM, a.Hq, a.B);
+  const dim3 gk((a.Lk + kBM - 1) / kBM, a.Hkv, a.B);
+  if (a.causal) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), gq, dim3(kBT), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), gk, dim3(kBT), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), gq, dim3(kBT), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), gk, dim3(kBT), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_dtype(const BwdArgs& a, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_bwd_t<T, 64>(a, stream);
+    case 128: return launch_bwd_t<T, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int bwd_padded_rows(int Lq) { return (Lq + kTile - 1) / kTile * kTile; }
+
+size_t bwd_workspace_bytes(int B, int Hq, int Lq) {
+  return 2 * (size_t)B * Hq * bwd_padded_rows(Lq) * sizeof(float);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  return a.bf16 ? launch_bwd_dtype<bf16_t>(a, stream) : launch_bwd_dtype<f16_t>(a, stream);
+}
+
+}  // namespace fa

@@ -47,7 +47,28 @@ struct DecodeArgs {
   const float* v_scales = nullptr;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Lq, Lk, D;
+  float scale;
+  int causal;
+  int win_left, win_right;
+  void* workspace;
+  int bf16;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+size_t bwd_workspace_bytes(int B, int Hq, int Lq);
+int bwd_padded_rows(int Lq);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 

@@ -192,6 +192,46 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
                           void* workspace, size_t workspace_bytes, fa_dtype dtype,
                           hipStream_t stream);
 
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two float32
+ * arrays [B, Hq, Lq rounded up to a multiple of 32] (per-row lse * log2(e)
+ * and rowsum(dO * O)).  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Lq);
+
+/*
+ * fa_bwd -- gradients dQ, dK, dV of fa_fwd / fa_fwd_ex (dense batch) given
+ * the gradient dO of its output, from the forward's q, k, v, o and lse.
+ *
+ * The gradient of the forward's definition: with P_ij = exp(scale q_i.k_j -
+ * lse_i) on the keys row i may see, dV_j = sum_i P_ij dO_i, dS_ij = P_ij
+ * (dO_i.v_j - dO_i.o_i), dQ_i = scale sum_j dS_ij k_j, dK_j = scale sum_i
+ * dS_ij q_i; grouped K/V heads sum their query heads' dK, dV.  The pages only
+ * report training with the method ("FlashAttention-2 (TH)",
+ * systems-analysis.info, performance) and pair every forward operator with a
+ * backward ("5 years, 10K stars: xformers", cloud.tencent.com); the formulas
+ * are calculus on the forward.  No atomics: results are bitwise reproducible.
+ *
+ *   q, o, dout  device [B, Lq, Hq, D] (dtype), 16-byte aligned.
+ *   k, v        device [B, Lk, Hkv, D] (dtype), 16-byte aligned.
+ *   lse         device float32 [B, Hq, Lq], as written by the forward.
+ *   dq          device [B, Lq, Hq, D] (dtype), written.
+ *   dk, dv      device [B, Lk, Hkv, D] (dtype), written (summed over each
+ *               K/V head's query heads).
+ *   D           64 or 128 (256: FA_ERR_UNSUPPORTED -- the two D x 32 fp32
+ *               accumulators per wave do not fit the register file).
+ *   causal, window_left, window_right, scale: as in fa_fwd_ex; must be the
+ *               forward's.
+ *   workspace   fa_bwd_workspace_size(B, Hq, Lq) bytes, 16-byte aligned,
+ *               caller-owned, contents need not be initialised.
+ *   B*Lq*Hq and B*Lk*Hkv below 2^31, Hq*D and Hkv*D below 2^25.
+ * Returns FA_OK once the three kernels are enqueued.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq,
+                 int Lk, int D, float scale, int causal, int window_left, int window_right,
+                 void* workspace, size_t workspace_bytes, fa_dtype dtype, hipStream_t stream);
+
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

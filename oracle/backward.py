@@ -76,10 +76,13 @@ def _head_backward(qh, kh, vh, doh, scale, causal, window, row_block, bounds):
         dq[r0:r1] = scale * (ds @ kh)
         dk += scale * (ds.T @ qh[r0:r1])
         if bounds:
+            # magnitudes for error bounds: |terms| of each sum, plus the
+            # sensitivity of dS to an error in D_i (relative to sum_d |dO O|)
             abs_v += p.T @ np.abs(do)
-            ads = np.abs(ds)
-            abs_q[r0:r1] = abs(scale) * (ads @ np.abs(kh))
-            abs_k += abs(scale) * (ads.T @ np.abs(qh[r0:r1]))
+            abs_d = np.abs(do * (p @ vh)).sum(axis=1)
+            wgt = np.abs(ds) + p * abs_d[:, None]
+            abs_q[r0:r1] = abs(scale) * (wgt @ np.abs(kh))
+            abs_k += abs(scale) * (wgt.T @ np.abs(qh[r0:r1]))
     return dq, dk, dv, abs_q, abs_k, abs_v
 
 
@@ -93,6 +96,12 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, *, window=(-1, -1
     bounds).  ``kv_heads`` optionally restricts the work to a list of
     (b, kv head) pairs: their dK, dV and the dQ of their query heads are
     computed, everything else is NaN.
+
+    The bounds are abs_dv_j = sum_i P_ij |dO_i|, abs_dq_i = |scale| sum_j
+    w_ij |k_j| and abs_dk_j = |scale| sum_i w_ij |q_i| with w_ij = |dS_ij| +
+    P_ij sum_d |dO_id O_id| (the second part: how much dS moves when D_i is
+    off by a relative amount).  A kernel whose P, dS and D carry relative
+    errors e has gradient errors of about e times these.
     """
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
     B, Lq, Hq, D = q.shape

@@ -36,8 +36,8 @@ def lib():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_ex", "fa_decode", "fa_decode_paged", "fa_decode_workspace_size",
-         "fa_last_error", "fa_info"])
+        ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_decode",
+         "fa_decode_paged", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -185,3 +185,33 @@ def dec_paged(**kw):
 def test_decode_paged_rejects(lib, kw, status, text):
     assert dec_paged(**kw) == status
     assert text in _abi.fa_last_error()
+
+
+def bwd(**kw):
+    a = dict(q=A16, k=A16, v=A16, o=A16, do=A16, lse=A16, dq=A16, dk=A16, dv=A16, B=1, Hq=2, Hkv=1,
+             Lq=8, Lk=8, D=64, scale=0.125, causal=1, wl=-1, wr=-1, ws=A16, ws_bytes=1 << 30,
+             dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_bwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(do=None), _abi.FA_ERR_INVALID_ARGUMENT, "dout is NULL"),
+    (dict(dk=A16 + 8), _abi.FA_ERR_INVALID_ARGUMENT, "dk is not 16-byte aligned"),
+    (dict(ws=None), _abi.FA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
+    (dict(ws_bytes=16), _abi.FA_ERR_INVALID_ARGUMENT, "needs"),
+    (dict(D=256), _abi.FA_ERR_UNSUPPORTED, "backward head_dim 256"),
+    (dict(Hq=3, Hkv=2), _abi.FA_ERR_INVALID_ARGUMENT, "not a multiple"),
+    (dict(Lk=0), _abi.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1"),
+    (dict(scale=float("inf")), _abi.FA_ERR_INVALID_ARGUMENT, "not finite"),
+    (dict(Hq=1 << 20, Hkv=1 << 20, D=64), _abi.FA_ERR_INVALID_ARGUMENT, "2^25"),
+])
+def test_bwd_rejects(lib, kw, status, text):
+    assert bwd(**kw) == status
+    assert text in _abi.fa_last_error()
+
+
+def test_bwd_workspace_size(lib):
+    assert _abi.fa_bwd_workspace_size(2, 3, 33) == 2 * 2 * 3 * 64 * 4
+    assert _abi.fa_bwd_workspace_size(1, 1, 32) == 2 * 32 * 4
+    assert _abi.fa_bwd_workspace_size(0, 1, 32) == 0
