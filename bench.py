@@ -53,9 +53,10 @@ def parse():
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--with-copy", type=int, default=0, metavar="MIB",
                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
-    p.add_argument("--only", choices=["prefill", "decode", "masks", "paged"], default=None,
-                   help="masks / paged: time only the structured-mask prefill or the paged "
-                        "decode workloads (one JSON line)")
+    p.add_argument("--only", choices=["prefill", "decode", "masks", "paged", "bwd"], default=None,
+                   help="masks / paged / bwd: time only the structured-mask prefill, the paged "
+                        "decode or the backward workloads (one JSON line)")
+    p.add_argument("--no-bwd", action="store_true", help="skip the backward workload")
     p.add_argument("--paged-format", choices=["native", "k8", "kv8"], default=None,
                    help="time only this paged-cache format")
     p.add_argument("--no-paged", action="store_true",
@@ -249,6 +250,51 @@ def time_paged(fmt, dev, reps=10, warmup=3):
                          "traffic": traffic}}
 
 
+def time_bwd(dev, reps=10, warmup=3):
+    """fa_bwd (prep + dQ + dK/dV kernels) on the Llama-2-7B-shaped causal
+    workload, fed by one untimed fa_fwd: mean time (HIP events on the launch
+    stream) and algorithmic TFLOP/s (10*D per allowed pair per query head:
+    the S, dP, dV, dQ and dK products)."""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import flash_attn_bwd, flash_attn_fwd
+
+    cfg = W.PREFILL["llama7b"]
+    q, k, v = (t.to(dev) for t in W.prefill_inputs(cfg))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(cfg.seed + 100)).to(
+        cfg.dtype).to(dev)
+    sc = float(np.float32(cfg.scale))
+    o, lse = flash_attn_fwd(q, k, v, softmax_scale=sc, causal=cfg.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    from exact_tiled_attention_fa_amd import _abi
+    ws = torch.empty((_abi.fa_bwd_workspace_size(cfg.B, cfg.Hq, cfg.L),), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: flash_attn_bwd(q, k, v, o, lse, do, softmax_scale=sc, causal=cfg.causal, dq=dq,
+                                 dk=dk, dv=dv, workspace=ws)
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    mean = float(np.mean(ms))
+    flops = cfg.flops() // 4 * 10
+    tf = flops / (mean * 1e-3) / 1e12
+    return {"workload": "llama7b causal backward B=4 Hq=Hkv=32 L=4096 D=128 bf16 (dQ, dK, dV)",
+            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
+                   "min": round(float(np.min(ms)), 5)},
+            "alg_flops_per_launch": flops, "value": round(tf, 3), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}}
+
+
 def time_masked(cfg, dev, reps=10, warmup=3):
     """Mean launch time (ms, HIP events on the launch stream) of one
     structured-mask workload, and its algorithmic TFLOP/s."""
@@ -333,6 +379,13 @@ def main():
     do_dec = args.only in (None, "decode")
     masks = {n: c for n, c in W.MASKED.items() if args.mask in (None, n)}
     paged_fmts = [f for f in PAGED_FORMATS if args.paged_format in (None, f)]
+    if args.only == "bwd":
+        print("# backward workload", file=sys.stderr, flush=True)
+        res = time_bwd(dev)
+        if args.with_copy:
+            copy_calibration(args.with_copy, dev)
+        print(json.dumps({"backward": res, "lib": info}), flush=True)
+        return
     if args.only == "paged":
         print("# paged decode workloads", file=sys.stderr, flush=True)
         res = {f: time_paged(f, dev) for f in paged_fmts}
@@ -440,6 +493,9 @@ def main():
     if do_dec and not args.no_paged:
         print("# paged decode workloads", file=sys.stderr, flush=True)
         out["decode"]["paged"] = {f: time_paged(f, dev) for f in paged_fmts}
+    if do_pf and not args.no_bwd:
+        print("# backward workload", file=sys.stderr, flush=True)
+        out["backward"] = time_bwd(dev)
     if do_pf and not args.no_masks:
         print("# structured-mask workloads", file=sys.stderr, flush=True)
         out["masks"] = {name: time_masked(cfg, dev) for name, cfg in masks.items()}

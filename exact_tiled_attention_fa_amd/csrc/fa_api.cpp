@@ -266,8 +266,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     return fail(FA_ERR_INVALID_ARGUMENT, "Hq * D and Hkv * D must be < 2^25");
   if ((long long)B * Lq * Hq > 0x7fffffffLL || (long long)B * Lk * Hkv > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
-  if (B > 65535 || Hq > 65535)
-    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (B or Hq exceeds 65535)");
+  if (((long long)Lq + 127) / 128 * B * Hq > 0x7fffffffLL ||
+      ((long long)Lk + 127) / 128 * B * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (L/128 * B * H > 2^31-1)");
   const long long span = (long long)B * Lq + (long long)B * Lk;
   const bool windowed = window_left >= 0 || window_right >= 0;
   if (windowed && span > (1LL << 30))

@@ -192,9 +192,14 @@ void bwd_dq_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
+  // Blocks run in index order; the query tile is the slowest index, heaviest
+  // (last, under a causal mask) first, so the lightest blocks come last.
   const int nqt = (Lq + kBM - 1) / kBM;
-  const int qt = CAUSAL ? nqt - 1 - (int)blockIdx.x : (int)blockIdx.x;  // heaviest first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int bh_n = Hq * p.B;
+  const int tslot = (int)blockIdx.x / bh_n;
+  const int bh = (int)blockIdx.x - tslot * bh_n;
+  const int qt = CAUSAL ? nqt - 1 - tslot : tslot;
+  const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / (Hq / p.Hkv);
   const int shift = Lk - Lq;
   const int q0 = qt * kBM, qw0 = q0 + kBR * w, qrow = qw0 + l32;
@@ -331,7 +336,12 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int kt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;  // kt ascending: heaviest first
+  // The key tile is the slowest block index, ascending: under a causal mask
+  // the first key tiles see the most queries, so the heaviest blocks go first.
+  const int bh_n = Hkv * p.B;
+  const int kt = (int)blockIdx.x / bh_n;
+  const int bkv = (int)blockIdx.x - kt * bh_n;
+  const int b = bkv / Hkv, kvh = bkv - b * Hkv;
   const int shift = Lk - Lq;
   const int k0 = kt * kBM, kw0 = k0 + kBR * w, key = kw0 + l32;
   const int k_last = min(k0 + kBM, Lk) - 1;
@@ -511,8 +521,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gq((a.Lq + kBM - 1) / kBM, a.Hq, a.B);
-  const dim3 gk((a.Lk + kBM - 1) / kBM, a.Hkv, a.B);
+  const dim3 gq((unsigned)((long)((a.Lq + kBM - 1) / kBM) * a.Hq * a.B));
+  const dim3 gk((unsigned)((long)((a.Lk + kBM - 1) / kBM) * a.Hkv * a.B));
   if (a.causal) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), gq, dim3(kBT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
