@@ -24,6 +24,9 @@ Contents
 ``backward.attention_bwd_ref``
     The gradients of the definition with respect to Q, K and V given dO
     (the chain rule through scores, row softmax and weighted sum), float64.
+``fp8.attention_fp8_ref`` / ``fp8.e4m3_decode``
+    The forward on e4m3-coded Q, K and V (transposed) with per-tensor
+    descales: exact decoding of the codes, then ``attention_ref``.
 ``online.online_attention_ref`` / ``online.split_combine_ref``
     The blockwise online-softmax recurrence and the logsumexp merge of
     key-chunk summaries, restated in float64 from the pages.  These are
@@ -38,11 +41,14 @@ than itself: a 40-digit ``decimal`` brute force, PyTorch's fp64 CPU
 from .attention import (attention_ref, causal_allowed, decode_paged_ref, decode_ref, key_bounds,
                         varlen_ref)
 from .backward import attention_bwd_ref
+from .fp8 import attention_fp8_ref, e4m3_decode
 from .online import online_attention_ref, split_combine_ref
 
 __all__ = [
     "attention_ref",
     "attention_bwd_ref",
+    "attention_fp8_ref",
+    "e4m3_decode",
     "decode_ref",
     "decode_paged_ref",
     "causal_allowed",
