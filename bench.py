@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s (causal prefill) + decode HBM GB/s, % roofline"
 PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X published HBM3E bandwidth
+PEAK_MFMA_FP8_TFLOPS = 5000.0   # MI355X published dense fp8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_fa_amd", "csrc")
 
@@ -53,10 +54,12 @@ def parse():
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--with-copy", type=int, default=0, metavar="MIB",
                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
-    p.add_argument("--only", choices=["prefill", "decode", "masks", "paged", "bwd"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "masks", "paged", "bwd", "fp8"],
+                   default=None,
                    help="masks / paged / bwd: time only the structured-mask prefill, the paged "
                         "decode or the backward workloads (one JSON line)")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward workload")
+    p.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward workload")
     p.add_argument("--paged-format", choices=["native", "k8", "kv8"], default=None,
                    help="time only this paged-cache format")
     p.add_argument("--no-paged", action="store_true",
@@ -120,7 +123,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> di
         return statistics.median(v) if v else None
 
     is_copy = lambda n: "copybuffer" in n.lower()  # the runtime's device-to-device copy kernel
-    is_fwd = lambda n: "fwd_kernel<fa::bf16_t, 128, true>" in n
+    if key == "fp8":
+        is_fwd = lambda n: "fwd_fp8_kernel<128, fa::bf16_t, true>" in n
+    else:
+        is_fwd = lambda n: "fwd_kernel<fa::bf16_t, 128, true>" in n
     is_split = lambda n: "decode_split_kernel<fa::bf16_t, 128," in n  # one cache format per run
     is_comb = lambda n: "decode_combine_kernel<fa::bf16_t, 128>" in n
     fr, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
@@ -136,7 +142,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> di
            "copy_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
     f_k, w_k = med(fr, is_fwd), med(wr, is_fwd)
     if f_k is not None and w_k is not None and not (key or "").startswith("paged:"):
-        out[key or "fwd_kernel"] = {"source_digest": source_digest(["fa_fwd.hip", "fa_common.hpp"]),
+        src = ["fa_fwd_fp8.hip" if key == "fp8" else "fa_fwd.hip", "fa_common.hpp"]
+        out[key or "fwd_kernel"] = {"source_digest": source_digest(src),
                              "fetch_kib": f_k, "write_kib": w_k,
                              "bytes_per_launch": int((f_k * ff + w_k * fw) * 1024)}
     parts = [(med(fr, p), med(wr, p)) for p in (is_split, is_comb)]
@@ -295,6 +302,52 @@ def time_bwd(dev, reps=10, warmup=3):
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}}
 
 
+def time_fp8(dev, reps=10, warmup=3):
+    """fa_fwd_fp8 on the Llama-2-7B-shaped causal workload with e4m3 Q, K, V:
+    mean time (HIP events on the launch stream) and algorithmic TFLOP/s
+    (4*D per allowed pair per query head) against the fp8 MFMA peak."""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd_fp8
+
+    cfg = W.PREFILL["llama7b"]
+    q8, k8, vt8, ds = W.fp8_inputs(cfg.B, cfg.L, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, cfg.seed)
+    q8, k8, vt8 = q8.to(dev), k8.to(dev), vt8.to(dev)
+    o = torch.empty((cfg.B, cfg.L, cfg.Hq, cfg.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.L), dtype=torch.float32, device=dev)
+    sc = float(np.float32(cfg.scale))
+    run = lambda: flash_attn_fwd_fp8(q8, k8, vt8, q_descale=ds, k_descale=ds, v_descale=ds,
+                                     softmax_scale=sc, causal=True, out=o, lse=lse)
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    mean = float(np.mean(ms))
+    tf = cfg.flops() / (mean * 1e-3) / 1e12
+    return {"workload": "llama7b causal prefill B=4 Hq=Hkv=32 L=4096 D=128, e4m3 Q/K/V "
+                        "(per-tensor descale), bf16 O",
+            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
+                   "min": round(float(np.min(ms)), 5)},
+            "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3), "unit": "TFLOP/s",
+            # Q, K, V one byte per element read once, O (bf16) and lse written once
+            "alg_bytes_per_launch": cfg.B * cfg.L * (3 * cfg.Hq * cfg.D + 2 * cfg.Hkv * cfg.D)
+            + cfg.B * cfg.Hq * cfg.L * 4,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_FP8_TFLOPS, 4),
+                         "traffic": traffic_for("fp8", source_digest(["fa_fwd_fp8.hip",
+                                                                      "fa_common.hpp"]))},
+            "kernel": "fwd_fp8_kernel<128, bf16_t, true>"}
+
+
 def time_masked(cfg, dev, reps=10, warmup=3):
     """Mean launch time (ms, HIP events on the launch stream) of one
     structured-mask workload, and its algorithmic TFLOP/s."""
@@ -379,6 +432,13 @@ def main():
     do_dec = args.only in (None, "decode")
     masks = {n: c for n, c in W.MASKED.items() if args.mask in (None, n)}
     paged_fmts = [f for f in PAGED_FORMATS if args.paged_format in (None, f)]
+    if args.only == "fp8":
+        print("# fp8 forward workload", file=sys.stderr, flush=True)
+        res = time_fp8(dev)
+        if args.with_copy:
+            copy_calibration(args.with_copy, dev)
+        print(json.dumps({"fp8": res, "lib": info}), flush=True)
+        return
     if args.only == "bwd":
         print("# backward workload", file=sys.stderr, flush=True)
         res = time_bwd(dev)
@@ -493,6 +553,9 @@ def main():
     if do_dec and not args.no_paged:
         print("# paged decode workloads", file=sys.stderr, flush=True)
         out["decode"]["paged"] = {f: time_paged(f, dev) for f in paged_fmts}
+    if do_pf and not args.no_fp8:
+        print("# fp8 forward workload", file=sys.stderr, flush=True)
+        out["fp8"] = time_fp8(dev)
     if do_pf and not args.no_bwd:
         print("# backward workload", file=sys.stderr, flush=True)
         out["backward"] = time_bwd(dev)

@@ -83,6 +83,47 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, softmax
     return out, lse
 
 
+def _as_bytes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise ValueError(f"{name} must hold e4m3 codes (torch.float8_e4m3fn or uint8)")
+    return t
+
+
+def flash_attn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, *, q_descale: float,
+                       k_descale: float, v_descale: float, softmax_scale=None,
+                       causal: bool = False, window=(-1, -1), out_dtype=torch.bfloat16, out=None,
+                       lse=None):
+    """FP8 forward.  q8 [B,Lq,Hq,D], k8 [B,Lk,Hkv,D] e4m3; vt8 [B,Hkv,D,S]
+    e4m3 (V transposed, S a multiple of 64 >= Lk, columns past Lk zero).  The
+    real values are code * descale.  Returns (o [B,Lq,Hq,D] in out_dtype, lse
+    [B,Hq,Lq])."""
+    for t, n in ((q8, "q8"), (k8, "k8"), (vt8, "vt8")):
+        _check_dev(t, n)
+    q8, k8, vt8 = _as_bytes(q8, "q8"), _as_bytes(k8, "k8"), _as_bytes(vt8, "vt8")
+    if q8.dim() != 4 or k8.dim() != 4 or vt8.dim() != 4:
+        raise ValueError("expected q8 [B,Lq,Hq,D], k8 [B,Lk,Hkv,D], vt8 [B,Hkv,D,S]")
+    B, Lq, Hq, D = q8.shape
+    Bk, Lk, Hkv, Dk = k8.shape
+    if Bk != B or Dk != D or tuple(vt8.shape[:3]) != (B, Hkv, D):
+        raise ValueError("shape mismatch between q8, k8 and vt8")
+    if out_dtype not in _DTYPES:
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty((B, Lq, Hq, D), dtype=out_dtype, device=q8.device) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q8.device)
+    st = _abi.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), B, Hq, Hkv, Lq, Lk, D, vt8.shape[3], scale,
+                         float(q_descale), float(k_descale), float(v_descale),
+                         1 if causal else 0, int(window[0]), int(window[1]), _DTYPES[out_dtype],
+                         _stream_handle(q8.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
+    return out, lse
+
+
 def flash_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                    lse: torch.Tensor, dout: torch.Tensor, *, softmax_scale=None,
                    causal: bool = False, window=(-1, -1), dq=None, dk=None, dv=None,

@@ -115,6 +115,52 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   return ok();
 }
 
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Lq, int Lk, int D, int vt_stride, float scale,
+                     float q_descale, float k_descale, float v_descale, int causal,
+                     int window_left, int window_right, fa_dtype out_dtype, hipStream_t stream) {
+  FA_TRY(check_ptr(q8, "q8"));
+  FA_TRY(check_ptr(k8, "k8"));
+  FA_TRY(check_ptr(vt8, "vt8"));
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(lse, "lse"));
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || D < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d)", B, Hq, Hkv, Lq, Lk, D);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!(isfinite(q_descale) && isfinite(k_descale) && isfinite(v_descale) && q_descale > 0.f &&
+        k_descale > 0.f && v_descale > 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "descales must be finite and > 0");
+  if (out_dtype != FA_F16 && out_dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)out_dtype);
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 head_dim %d not in {64, 128}", D);
+  if (vt_stride < Lk || vt_stride % 64 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "vt_stride=%d must be a multiple of 64 and >= Lk=%d",
+                vt_stride, Lk);
+  if ((long long)D * vt_stride >= (1LL << 32))
+    return fail(FA_ERR_INVALID_ARGUMENT, "D * vt_stride must be < 2^32");
+  if ((long long)Hkv * D >= (1LL << 25) || (long long)Hq * D >= (1LL << 25))
+    return fail(FA_ERR_INVALID_ARGUMENT, "Hq * D and Hkv * D must be < 2^25");
+  if ((long long)B * Lq * Hq > 0x7fffffffLL || (long long)B * Lk * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
+  if (((long long)Lq + 127) / 128 * B * Hq > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (Lq/128 * B * Hq > 2^31-1)");
+  const long long span = (long long)B * Lq + (long long)B * Lk;
+  const bool windowed = window_left >= 0 || window_right >= 0;
+  if (windowed && span > (1LL << 30))
+    return fail(FA_ERR_INVALID_ARGUMENT, "windowed attention needs query + key rows <= 2^30");
+  fa::Fp8Args a{q8, k8, vt8, o, lse, B, Hq, Hkv, Lq, Lk, D, vt_stride, scale, q_descale,
+                k_descale, v_descale, causal ? 1 : 0,
+                (window_left < 0 || window_left >= span) ? -1 : window_left,
+                (window_right < 0 || window_right >= span) ? -1 : window_right,
+                out_dtype == FA_BF16 ? 1 : 0};
+  hipError_t e = fa::launch_fwd_fp8(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_fp8 launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t fa_decode_workspace_size(int B, int Hq, int D, int num_splits) {
   if (B < 1 || Hq < 1 || D < 1 || num_splits < 1 || num_splits > 64) return 0;
   return fa::decode_workspace_bytes(B, Hq, D, num_splits);

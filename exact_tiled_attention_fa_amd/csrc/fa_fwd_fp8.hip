@@ -1,0 +1,343 @@
+// FP8 (e4m3) forward: the tiled online-softmax forward with Q, K and V stored
+// as 8-bit e4m3 codes plus one float descale each, on gfx950's double-rate
+// v_mfma_f32_32x32x64_f8f6f4.
+//
+// The FP8 variant of the method is the FlashAttention-3 item of
+// "FlashAttention-2 (TH)" (systems-analysis.info); the page gives neither the
+// format nor the scaling.  Read here as OCP e4m3 codes with per-tensor
+// descales (the real value is code * descale), V supplied transposed
+// ([B, Hkv, D, stride], keys contiguous per dimension, as written by the
+// quantisation step), and P rounded to e4m3 for the PV product.
+//
+// gfx950 mapping (one workgroup = 4 wave64 = 128 query rows, 64-key tiles):
+//   * S^T = K Q^T: two 32x32 blocks per tile, each D/64 MFMAs of k = 64 dims.
+//     A = 32 K rows from LDS, B = Q^T in registers (32 bytes per lane per
+//     MFMA).  The A rows are taken in the order 16h + 4g + i -> accumulator
+//     row 8g + 4h + i, so each lane's 16 scores of a block are 16 consecutive
+//     keys (16h .. 16h+15 of the block).
+//   * O^T += V^T P^T: one MFMA (k = 64 keys) per 32 head dimensions.  B =
+//     P^T straight from the score registers, scaled by 256 (so the e4m3
+//     rounding stays clear of subnormals) and packed with v_cvt_pk_fp8_f32;
+//     A = 32 bytes of one V^T row (two ds_read_b128 of keys 16h.. and
+//     32+16h..), matching the keys each lane's P bytes carry.  The two
+//     operands of the f8f6f4 MFMA share their k layout, so matching byte
+//     positions is all that is needed.
+//   * Online softmax as in the 16-bit forward, with the lazy rescale limited
+//     to a factor of 2^0.5 so that 256 * P stays below e4m3's 448.  The row sum
+//     adds the unrounded fp32 probabilities.
+//   * K and V^T tiles stream HBM -> LDS with LDS-direct copies, two stages.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kPW = 4;            // waves per workgroup
+constexpr int kPT = kPW * 64;     // threads
+constexpr int kPR = 32;           // query rows per wave
+constexpr int kPBM = kPW * kPR;   // query rows per workgroup
+constexpr int kPBN = 64;          // keys per tile
+constexpr int kXcd = 8;
+
+struct Fp8Params {
+  const uint8_t* Q;
+  const uint8_t* K;
+  const uint8_t* VT;
+  uint16_t* O;
+  float* LSE;
+  int B, Hq, Hkv, Lq, Lk, vt_stride;
+  int win_left, win_right;
+  float scale2;  // |scale * q_descale * k_descale| * log2(e)
+  float thr;     // lazy-rescale slack in raw score units
+  float oscale;  // v_descale / 256
+  uint32_t qxor; // sign flip of q for a negative scale
+};
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // e4m3 x e4m3 (format code 0 for both operands), no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// K tile rows are D bytes (D/16 chunks); XOR on the chunk index so that the
+// 8 rows {0..3, 16..19} (+4, +8, ...) read together hit distinct banks.
+template <int D> __device__ __forceinline__ int swz_k8(int r) {
+  return D >= 128 ? ((r & 3) | (((r >> 4) & 1) << 2)) : (r & 3);
+}
+// V^T tile rows are 64 bytes (4 chunks).
+__device__ __forceinline__ int swz_v8(int d) { return (d >> 1) & 3; }
+
+__device__ __forceinline__ i32x8 cat(u32x4 a, u32x4 b) {
+  return (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2],
+                 (int)b[3]};
+}
+
+template <int D, typename OT, bool CAUSAL>
+__global__ __launch_bounds__(kPT, 2)
+void fwd_fp8_kernel(const Fp8Params prm) {
+  constexpr int KT = kPBN * D;   // bytes per K tile
+  constexpr int VTB = D * kPBN;  // bytes per V^T tile
+  constexpr int CK = D / 16;     // 16-byte chunks per K row
+  constexpr int NK = kPBN * CK / kPT;
+  constexpr int NV = D * 4 / kPT;
+  static_assert(NK >= 1 && NV >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t sK0[KT];
+  __shared__ __attribute__((aligned(16))) uint8_t sV0[VTB];
+  __shared__ __attribute__((aligned(16))) uint8_t sK1[KT];
+  __shared__ __attribute__((aligned(16))) uint8_t sV1[VTB];
+
+  const int B = prm.B, Hq = prm.Hq, Hkv = prm.Hkv, Lq = prm.Lq, Lk = prm.Lk;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  // Block -> (b, h, query tile): XCD x takes query heads [x*Hq/8, (x+1)*Hq/8)
+  // of every sequence when Hq is a multiple of 8, else a contiguous slice of
+  // the list; heaviest query tile first.
+  const int nqt = (Lq + kPBM - 1) / kPBM;
+  const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
+  int b, h, qt;
+  if (Hq % kXcd == 0) {
+    const int hx = Hq / kXcd;
+    const int per_b = hx * nqt;
+    b = slot / per_b;
+    const int r = slot - b * per_b;
+    const int hh = r / nqt;
+    qt = r - hh * nqt;
+    h = xcd * hx + hh;
+  } else {
+    const int N = nqt * B * Hq;
+    const int item = xcd * (N / kXcd) + min(xcd, N % kXcd) + slot;
+    const int bhi = item / nqt;
+    qt = item - bhi * nqt;
+    b = bhi / Hq;
+    h = bhi - b * Hq;
+  }
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int kvh = h / (Hq / Hkv);
+  const int shift = Lk - Lq;
+  const int q0 = qt * kPBM, qw0 = q0 + kPR * w, qrow = qw0 + l32;
+  const int wl = prm.win_left, wr = prm.win_right;
+  auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
+  auto kmax = [&](int i) {
+    int hi = Lk - 1;
+    if (CAUSAL) hi = min(hi, i + shift);
+    if (wr >= 0) hi = min(hi, i + shift + wr);
+    return hi;
+  };
+
+  const long qstride = (long)Hq * D;
+  const int kstride = Hkv * D;
+  const uint8_t* Kb = prm.K + (long)b * Lk * kstride + (long)kvh * D;
+  const uint8_t* Vb = prm.VT + ((long)b * Hkv + kvh) * D * (long)prm.vt_stride;
+
+  // Q^T operand: lane holds query qrow, dims 64m + 32hf .. +31 for MFMA m.
+  i32x8 qf[D / 64];
+  {
+    const uint8_t* qr = prm.Q + ((long)b * Lq + min(qrow, Lq - 1)) * qstride + (long)h * D;
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m) {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(qr + 64 * m + 32 * hf) ^ prm.qxor;
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(qr + 64 * m + 32 * hf + 16) ^ prm.qxor;
+      qf[m] = cat(x0, x1);
+    }
+  }
+
+  const int q_last = min(q0 + kPBM, Lq) - 1;
+  const int wg_lo = kmin(q0), wg_hi = kmax(q_last);
+  const int t_first = wg_lo / kPBN;
+  const int ntiles = wg_hi >= wg_lo ? wg_hi / kPBN - t_first + 1 : 0;
+  const int qw_last = min(qw0 + kPR - 1, Lq - 1);
+  const bool wave_live = qw0 < Lq && kmax(qw_last) >= kmin(qw0);
+  const int first_live = wave_live ? kmin(qw0) / kPBN - t_first : ntiles;
+  const int last_live = wave_live ? kmax(qw_last) / kPBN - t_first : -1;
+  const int row_kmin = kmin(qrow), row_kmax = kmax(qrow);
+
+  // Loaders: LDS byte position 16 * P holds chunk P of the tile.
+  uint32_t koff[NK], voff[NV];
+  int krow[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int P = (i * kPW + wu) * 64 + lane;
+    const int r = P / CK, pc = P % CK;
+    krow[i] = r;
+    koff[i] = (uint32_t)(r * kstride + 16 * (pc ^ swz_k8<D>(r)));
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int P = (i * kPW + wu) * 64 + lane;
+    const int d = P >> 2, pc = P & 3;
+    voff[i] = (uint32_t)(d * prm.vt_stride + 16 * (pc ^ swz_v8(d)));
+  }
+  auto issue = [&](int t, uint8_t* dK, uint8_t* dV) {
+    const int j0 = t * kPBN;
+    const uint8_t* kbase = Kb + (long)j0 * kstride;
+    const bool whole = j0 + kPBN <= Lk;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      uint32_t o = koff[i];
+      if (!whole) o -= (uint32_t)(((j0 + krow[i]) - min(j0 + krow[i], Lk - 1)) * kstride);
+      load_lds16_off(kbase, o, dK + (i * kPW + wu) * 1024);
+    }
+    // V^T columns j0 .. j0+63 lie inside the row (stride a multiple of 64 >= Lk)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) load_lds16_off(Vb + j0, voff[i], dV + (i * kPW + wu) * 1024);
+  };
+
+  // A-operand rows of the S^T MFMA: lane i reads K row 16((i/4)%2) + 4(i/8) + i%4.
+  const int arow = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  float m_ref = -INFINITY, l_part = 0.f;
+  const float scale2 = prm.scale2, thr = prm.thr;
+
+  auto compute = [&](int u, const uint8_t* sK, const uint8_t* sV) {
+    const int j0 = (t_first + u) * kPBN;
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16){};
+      const int r = 32 * kb + arow;
+#pragma unroll
+      for (int m = 0; m < D / 64; ++m) {
+        const int c0 = 4 * m + 2 * hf;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sK + r * D + 16 * (c0 ^ swz_k8<D>(r)));
+        const u32x4 a1 =
+            *reinterpret_cast<const u32x4*>(sK + r * D + 16 * ((c0 + 1) ^ swz_k8<D>(r)));
+        s[kb] = mfma_fp8(cat(a0, a1), qf[m], s[kb]);
+      }
+    }
+    // score element r of block kb is key j0 + 32kb + 16hf + r
+    const bool whole = j0 >= kmin(qw_last) && j0 + kPBN - 1 <= kmax(qw0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (!whole) {
+          const int key = j0 + 32 * kb + 16 * hf + r;
+          if (key < row_kmin || key > row_kmax) s[kb][r] = -INFINITY;
+        }
+        mx = fmaxf(mx, s[kb][r]);
+      }
+    mx = max_halves(mx);
+    const bool upd = mx > m_ref + thr;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(upd) != 0, 0)) {
+      asm volatile("" ::: "memory");
+      const float m_new = upd ? mx : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast((m_ref - m_new) * scale2);
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      m_ref = m_new;
+    }
+    // P (x256 for the e4m3 rounding), packed four keys per dword: dword j of
+    // the B operand carries keys 16(j/4)... i.e. block j/4, elements 4(j%4)..+3.
+    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * scale2;
+    i32x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kb = j >> 2, r0 = 4 * (j & 3);
+      float p[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        p[t] = exp2_fast(__builtin_fmaf(s[kb][r0 + t], scale2, -mb));
+        l_part += p[t];
+      }
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.f, p[1] * 256.f, 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.f, p[3] * 256.f, wd, true);
+      pb[j] = wd;
+    }
+    // O^T += V^T P^T: A = V^T row d, keys 16hf .. +15 and 32+16hf .. +15
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = 32 * db + l32;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + d * kPBN + 16 * (hf ^ swz_v8(d)));
+      const u32x4 a1 =
+          *reinterpret_cast<const u32x4*>(sV + d * kPBN + 16 * ((2 + hf) ^ swz_v8(d)));
+      acc[db] = mfma_fp8(cat(a0, a1), pb, acc[db]);
+    }
+  };
+
+  if (ntiles > 0) {
+    issue(t_first, sK0, sV0);
+    for (int u = 0; u < ntiles; u += 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~0x0F00);
+      asm volatile("s_barrier" ::: "memory");
+      if (u + 1 < ntiles) issue(t_first + u + 1, sK1, sV1);
+      if (u >= first_live && u <= last_live) compute(u, sK0, sV0);
+      if (u + 1 >= ntiles) break;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~0x0F00);
+      asm volatile("s_barrier" ::: "memory");
+      if (u + 2 < ntiles) issue(t_first + u + 2, sK0, sV0);
+      if (u + 1 >= first_live && u + 1 <= last_live) compute(u + 1, sK1, sV1);
+    }
+  }
+
+  const float l = sum_halves(l_part);
+  const float inv = l > 0.f ? prm.oscale / l : 0.f;
+  if (qrow < Lq) {
+    uint16_t* out = prm.O + ((long)b * Lq + qrow) * qstride + (long)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 val = {Ops<OT>::pack2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
+                           Ops<OT>::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(out + 32 * db + 8 * g + 4 * hf) = val;
+      }
+    if (hf == 0)
+      prm.LSE[((long)b * Hq + h) * Lq + qrow] =
+          l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, typename OT>
+hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
+  Fp8Params p;
+  p.Q = (const uint8_t*)a.q;
+  p.K = (const uint8_t*)a.k;
+  p.VT = (const uint8_t*)a.vt;
+  p.O = (uint16_t*)a.o;
+  p.LSE = a.lse;
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.Lq = a.Lq;
+  p.Lk = a.Lk;
+  p.vt_stride = a.vt_stride;
+  p.win_left = a.win_left;
+  p.win_right = a.win_right;
+  const float sc = a.scale * a.q_descale * a.k_descale;
+  p.scale2 = fmaxf(fabsf(sc) * kLog2e, 1e-30f);
+  p.thr = 0.5f / p.scale2;
+  p.oscale = a.v_descale / 256.f;
+  p.qxor = sc < 0.f ? 0x80808080u : 0u;
+  const int nqt = (a.Lq + kPBM - 1) / kPBM;
+  const dim3 grid((unsigned)((long)nqt * a.B * a.Hq));
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, OT, true>), grid, dim3(kPT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, OT, false>), grid, dim3(kPT), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename OT>
+hipError_t launch_fp8_out(const Fp8Args& a, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_fp8_t<64, OT>(a, stream);
+    case 128: return launch_fp8_t<128, OT>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
+  return a.out_bf16 ? launch_fp8_out<bf16_t>(a, stream) : launch_fp8_out<f16_t>(a, stream);
+}
+
+}  // namespace fa

@@ -65,7 +65,21 @@ struct BwdArgs {
   int bf16;
 };
 
+struct Fp8Args {
+  const void* q;   // e4m3 [B, Lq, Hq, D]
+  const void* k;   // e4m3 [B, Lk, Hkv, D]
+  const void* vt;  // e4m3 [B, Hkv, D, vt_stride]
+  void* o;         // [B, Lq, Hq, D] bf16 / fp16
+  float* lse;      // [B, Hq, Lq]
+  int B, Hq, Hkv, Lq, Lk, D, vt_stride;
+  float scale, q_descale, k_descale, v_descale;
+  int causal;
+  int win_left, win_right;
+  int out_bf16;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int Hq, int Lq);
 int bwd_padded_rows(int Lq);

@@ -113,6 +113,35 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     int window_left, int window_right, fa_dtype dtype, hipStream_t stream);
 
 /*
+ * fa_fwd_fp8 -- the forward of fa_fwd_ex (dense batch, causal / window masks)
+ * on FP8 inputs: Q, K and V stored as OCP e4m3 codes, each with one float
+ * descale (the real value is code * descale), P rounded to e4m3 for the PV
+ * product, fp32 accumulation, O in bf16 or fp16.
+ *
+ * The FP8 variant is the FlashAttention-3 item of "FlashAttention-2 (TH)"
+ * (systems-analysis.info); the page fixes neither the format nor the
+ * scaling, read here as above.  Because P is rounded to e4m3 (relative error
+ * <= 2^-4), O is exact only to about 2^-4 * sum_j P_ij |v_j|; lse is computed
+ * from unrounded probabilities.
+ *
+ *   q8          device e4m3 [B, Lq, Hq, D], 16-byte aligned.
+ *   k8          device e4m3 [B, Lk, Hkv, D], 16-byte aligned.
+ *   vt8         device e4m3 [B, Hkv, D, vt_stride]: V transposed, key j of
+ *               dimension d at column j.  vt_stride is a multiple of 64,
+ *               >= Lk; columns Lk .. vt_stride-1 are read and must hold finite
+ *               codes (zeros), their probabilities being 0.
+ *   o, lse      as fa_fwd; o in out_dtype.
+ *   D           64 or 128.
+ *   scale       softmax scale applied to the real (descaled) scores.
+ *   q_descale, k_descale, v_descale   finite, > 0.
+ *   other arguments as in fa_fwd_ex.  D * vt_stride must be below 2^32.
+ */
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Lq, int Lk, int D, int vt_stride, float scale,
+                     float q_descale, float k_descale, float v_descale, int causal,
+                     int window_left, int window_right, fa_dtype out_dtype, hipStream_t stream);
+
+/*
  * fa_decode_workspace_size -- bytes of device workspace fa_decode needs for
  * these sizes: float32 partial outputs [B, Hq, num_splits, D] followed by
  * float32 partial logsumexps [B, Hq, num_splits].  Returns 0 for invalid sizes.

@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_decode",
+        ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_decode",
          "fa_decode_paged", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
 
 
@@ -215,3 +215,26 @@ def test_bwd_workspace_size(lib):
     assert _abi.fa_bwd_workspace_size(2, 3, 33) == 2 * 2 * 3 * 64 * 4
     assert _abi.fa_bwd_workspace_size(1, 1, 32) == 2 * 32 * 4
     assert _abi.fa_bwd_workspace_size(0, 1, 32) == 0
+
+
+def fp8(**kw):
+    a = dict(q=A16, k=A16, vt=A16, o=A16, lse=A16, B=1, Hq=2, Hkv=1, Lq=8, Lk=8, D=128, vts=64,
+             scale=0.1, qd=0.0625, kd=0.0625, vd=0.0625, causal=1, wl=-1, wr=-1,
+             dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_fwd_fp8(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(vt=None), _abi.FA_ERR_INVALID_ARGUMENT, "vt8 is NULL"),
+    (dict(vts=32), _abi.FA_ERR_INVALID_ARGUMENT, "vt_stride=32"),
+    (dict(vts=64, Lk=65), _abi.FA_ERR_INVALID_ARGUMENT, "vt_stride=64"),
+    (dict(qd=0.0), _abi.FA_ERR_INVALID_ARGUMENT, "descales"),
+    (dict(vd=float("nan")), _abi.FA_ERR_INVALID_ARGUMENT, "descales"),
+    (dict(D=256), _abi.FA_ERR_UNSUPPORTED, "fp8 head_dim 256"),
+    (dict(dtype=5), _abi.FA_ERR_UNSUPPORTED, "dtype 5"),
+    (dict(Hq=3, Hkv=2), _abi.FA_ERR_INVALID_ARGUMENT, "not a multiple"),
+])
+def test_fp8_rejects(lib, kw, status, text):
+    assert fp8(**kw) == status
+    assert text in _abi.fa_last_error()

@@ -1,0 +1,118 @@
+"""FP8 forward parity: libfa's fa_fwd_fp8 (through the C ABI) against the fp64
+oracle on the decoded e4m3 inputs.
+
+Error bound (derived from the arithmetic): the scores of e4m3 codes are exact
+products summed in fp32, so the only rounding beyond the 16-bit output is P's
+rounding to e4m3 for the PV product (relative error <= 2^-4 for the normal
+range; 256 * P keeps P >= 2^-14 normal).  Hence per element
+|dO| <= 2^-4 * sum_j P_ij |v_j| (the oracle's `mag`) + u_out |O| + 1e-4, and lse
+(from unrounded probabilities) keeps the 16-bit path's 1e-3 bound.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_fa_amd import workloads as W
+from gpu_util import f32, say, to64
+
+pytestmark = pytest.mark.gpu
+
+UNIT = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+
+
+def compare_fp8(o, lse, o_ref, l_ref, mag, out_dtype, what):
+    og, lg = to64(o), to64(lse)
+    o_ref, l_ref, mag = np.asarray(o_ref), np.asarray(l_ref), np.asarray(mag)
+    sel, lsel = ~np.isnan(o_ref), ~np.isnan(l_ref)
+    assert sel.any() and np.all(np.isfinite(og[sel])), f"{what}: non-finite output"
+    linf = lsel & np.isinf(l_ref)
+    assert np.array_equal(lg[linf], l_ref[linf]), f"{what}: empty-row lse differs"
+    lfin = lsel & ~np.isinf(l_ref)
+    tol = 2.0 ** -4 * mag[sel] + UNIT[out_dtype] * np.abs(o_ref[sel]) + 1e-4
+    err = np.abs(og[sel] - o_ref[sel])
+    ratio = float(np.max(err / tol))
+    dl = float(np.max(np.abs(lg[lfin] - l_ref[lfin]))) if lfin.any() else 0.0
+    rms = float(np.sqrt(np.mean(err ** 2)))
+    say(f"  {what}: max|dO|={err.max():.3e} rms {rms:.2e} worst err/bound={ratio:.3f} "
+        f"max|dlse|={dl:.2e}")
+    assert ratio <= 1.0, f"{what}: O error exceeds the bound by {ratio:.2f}x"
+    assert dl <= 1e-3, f"{what}: max|dlse| {dl:.3e} > 1e-3"
+
+
+def run_fp8(q8, k8, vt8, ds, scale, causal, window, out_dtype, dev):
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd_fp8
+
+    o, lse = flash_attn_fwd_fp8(q8.to(dev), k8.to(dev), vt8.to(dev), q_descale=ds, k_descale=ds,
+                                v_descale=ds, softmax_scale=scale, causal=causal, window=window,
+                                out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check(B, Lq, Lk, Hq, Hkv, D, causal, seed, gpu, *, window=(-1, -1), scale=None,
+          out_dtype=torch.bfloat16, q_scale=1.0, heads=None):
+    scale = f32(scale if scale is not None else D ** -0.5)
+    q8, k8, vt8, ds = W.fp8_inputs(B, Lq, Lk, Hq, Hkv, D, seed, q_scale=q_scale)
+    tag = f"fp8 B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} D={D} causal={causal} window={window}"
+    say(tag)
+    o, lse = run_fp8(q8, k8, vt8, ds, scale, causal, window, out_dtype, gpu)
+    o_ref, l_ref, mag = oracle.attention_fp8_ref(q8, k8, vt8, Lk, scale, ds, ds, ds, causal,
+                                                 heads=heads)
+    if window != (-1, -1):  # the fp8 oracle has no window argument: rebuild it from the definition
+        q = oracle.e4m3_decode(q8) * ds
+        k = oracle.e4m3_decode(k8) * ds
+        v = np.ascontiguousarray(oracle.e4m3_decode(vt8)[..., :Lk].transpose(0, 3, 1, 2)) * ds
+        o_ref, l_ref = oracle.attention_ref(q, k, v, scale, causal, window=window)
+        mag, _ = oracle.attention_ref(q, k, np.abs(v), scale, causal, window=window)
+    compare_fp8(o, lse, o_ref, l_ref, mag, out_dtype, tag)
+
+
+RAGGED = [(1, 1), (17, 17), (63, 63), (64, 64), (65, 65), (128, 128), (129, 129), (300, 300),
+          (1000, 1000), (1, 129), (65, 200), (200, 65), (129, 4097)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Lq,Lk", RAGGED, ids=[f"{a}x{b}" for a, b in RAGGED])
+def test_fp8_ragged(Lq, Lk, D, causal, gpu):
+    check(1, Lq, Lk, 4, 2, D, causal, seed=Lq * 13 + Lk + D, gpu=gpu)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_fp8_gqa(g, gpu):
+    check(2, 257, 257, 8, 8 // g, 128, True, seed=50 + g, gpu=gpu)
+
+
+@pytest.mark.parametrize("window", [(0, 0), (5, 3), (64, -1), (-1, 40)],
+                         ids=["w0_0", "w5_3", "w64_", "w_40"])
+def test_fp8_windows(window, gpu):
+    check(1, 300, 300, 4, 2, 128, True, seed=60 + window[0], gpu=gpu, window=window)
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
+def test_fp8_scales(scale, gpu):
+    check(1, 130, 130, 2, 1, 128, True, seed=70, gpu=gpu, scale=scale)
+
+
+def test_fp8_f16_output_and_large_logits(gpu):
+    check(1, 700, 700, 2, 2, 64, False, seed=71, gpu=gpu, out_dtype=torch.float16)
+    check(1, 700, 700, 2, 2, 128, True, seed=72, gpu=gpu, q_scale=4.0)
+
+
+def test_fp8_full_size_sampled(gpu):
+    """The Llama-2-7B-shaped causal workload (B=4, H=32, L=4096, D=128) in fp8,
+    in the launch the benchmark times; the oracle computes 3 whole heads."""
+    cfg = W.PREFILL["llama7b"]
+    heads = [(0, 0), (2, 17), (cfg.B - 1, cfg.Hq - 1)]
+    check(cfg.B, cfg.L, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, True, seed=cfg.seed, gpu=gpu, heads=heads)
+
+
+def test_fp8_deterministic(gpu):
+    q8, k8, vt8, ds = W.fp8_inputs(2, 1000, 1000, 8, 2, 128, 73)
+    a = run_fp8(q8, k8, vt8, ds, 0.088, True, (-1, -1), torch.bfloat16, gpu)
+    b = run_fp8(q8, k8, vt8, ds, 0.088, True, (-1, -1), torch.bfloat16, gpu)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
