@@ -337,7 +337,7 @@ const char* fa_last_error(void) { return g_err; }
 
 const char* fa_info(void) {
   return "arch=gfx950; head_dims={64,128,256}; dtypes={f16,bf16}; "
-         "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), 32-key tiles (64 at D=64), "
+         "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), 32-key tiles, "
          "mfma_f32_32x32x16, LDS-direct K/V with transpose reads, causal/window tile "
          "skip, block-diagonal packing, GQA; "
          "decode: split-KV, 4 wave64 per (chunk, kv head, 16 heads, sequence), 16-key steps, "
