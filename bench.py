@@ -140,6 +140,17 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> di
                      "dispatch, median over dispatches), each scaled by the factor that makes a "
                      f"plain {copy_mib} MiB device copy read and write exactly {copy_mib} MiB.",
            "copy_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
+    if key == "bwd":  # the three backward kernels of one fa_bwd call, summed
+        parts = [(med(fr, pr), med(wr, pr)) for pr in (
+            lambda n: "bwd_prep_kernel<fa::bf16_t, 128>" in n,
+            lambda n: "bwd_dq_kernel<fa::bf16_t, 128, true>" in n,
+            lambda n: "bwd_dkdv_kernel<fa::bf16_t, 128, true>" in n)]
+        if all(a is not None and b is not None for a, b in parts):
+            out["bwd"] = {"source_digest": source_digest(["fa_bwd.hip", "fa_common.hpp"]),
+                          "fetch_kib": sum(a for a, _ in parts),
+                          "write_kib": sum(b for _, b in parts),
+                          "bytes_per_launch": int(sum(a * ff + b * fw for a, b in parts) * 1024)}
+        return out
     f_k, w_k = med(fr, is_fwd), med(wr, is_fwd)
     if f_k is not None and w_k is not None and not (key or "").startswith("paged:"):
         src = ["fa_fwd_fp8.hip" if key == "fp8" else "fa_fwd.hip", "fa_common.hpp"]
@@ -294,12 +305,19 @@ def time_bwd(dev, reps=10, warmup=3):
     mean = float(np.mean(ms))
     flops = cfg.flops() // 4 * 10
     tf = flops / (mean * 1e-3) / 1e12
+    # Q, O, dO read and dQ written (query side), K, V read and dK, dV written,
+    # lse read: each once
+    nq, nk = cfg.B * cfg.L * cfg.Hq * cfg.D * 2, cfg.B * cfg.L * cfg.Hkv * cfg.D * 2
+    alg_bytes = 4 * nq + 4 * nk + cfg.B * cfg.Hq * cfg.L * 4
     return {"workload": "llama7b causal backward B=4 Hq=Hkv=32 L=4096 D=128 bf16 (dQ, dK, dV)",
             "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
                    "min": round(float(np.min(ms)), 5)},
-            "alg_flops_per_launch": flops, "value": round(tf, 3), "unit": "TFLOP/s",
+            "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
+            "value": round(tf, 3), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                         "traffic": traffic_for("bwd", source_digest(["fa_bwd.hip",
+                                                                      "fa_common.hpp"]))}}
 
 
 def time_fp8(dev, reps=10, warmup=3):

@@ -103,6 +103,23 @@ void bwd_prep_kernel(const BwdParams p) {
   }
 }
 
+// Block -> (head row, tile).  Blocks start in index order, so tile-major
+// order (tile 0 of every head, then tile 1, ...) puts the heaviest tiles first
+// and the lightest in the tail.  Block i runs on XCD i % 8; when the heads
+// split evenly over the 8 XCDs, XCD x takes the x-th contiguous slice of
+// heads and walks it tile-major, so the tiles it streams stay in its own L2.
+__device__ __forceinline__ void xcd_item(int rows, int& row, int& tile) {
+  const int i = (int)blockIdx.x;
+  if (rows % 8 == 0) {
+    const int per = rows / 8, xcd = i % 8, slot = i / 8;
+    tile = slot / per;
+    row = xcd * per + (slot - tile * per);
+  } else {
+    tile = i / rows;
+    row = i - tile * rows;
+  }
+}
+
 // LDS-direct copy of `rows` x D 16-bit elements (rows r0 .. r0+rows-1 of a
 // matrix with row stride `stride` elements; rows past `last` re-read `last`)
 // into an LDS tile, 16-byte chunks XOR-swizzled by row.  Every thread of the
@@ -192,14 +209,11 @@ void bwd_dq_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
-  // Blocks run in index order; the query tile is the slowest index, heaviest
-  // (last, under a causal mask) first, so the lightest blocks come last.
   const int nqt = (Lq + kBM - 1) / kBM;
-  const int bh_n = Hq * p.B;
-  const int tslot = (int)blockIdx.x / bh_n;
-  const int bh = (int)blockIdx.x - tslot * bh_n;
-  const int qt = CAUSAL ? nqt - 1 - tslot : tslot;
+  int bh, tt;
+  xcd_item(p.B * Hq, bh, tt);
   const int b = bh / Hq, h = bh - b * Hq;
+  const int qt = CAUSAL ? nqt - 1 - tt : tt;  // heaviest (last, under a causal mask) first
   const int kvh = h / (Hq / p.Hkv);
   const int shift = Lk - Lq;
   const int q0 = qt * kBM, qw0 = q0 + kBR * w, qrow = qw0 + l32;
@@ -336,11 +350,9 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
-  // The key tile is the slowest block index, ascending: under a causal mask
-  // the first key tiles see the most queries, so the heaviest blocks go first.
-  const int bh_n = Hkv * p.B;
-  const int kt = (int)blockIdx.x / bh_n;
-  const int bkv = (int)blockIdx.x - kt * bh_n;
+  // Key tiles ascending: under a causal mask the first see the most queries.
+  int bkv, kt;
+  xcd_item(p.B * Hkv, bkv, kt);
   const int b = bkv / Hkv, kvh = bkv - b * Hkv;
   const int shift = Lk - Lq;
   const int k0 = kt * kBM, kw0 = k0 + kBR * w, key = kw0 + l32;
