@@ -52,7 +52,6 @@ namespace fa {
 namespace {
 
 constexpr int kNT = kFwdWaves * 64;
-constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 
 // Keys per KV tile.  The pipelined loop keeps two score tiles, the packed
 // probabilities, the output accumulator and Q in registers; at D >= 128 a
@@ -100,6 +99,7 @@ struct FwdParams {
   int win_left, win_right;  // < 0: unbounded
   float scale2, thr;
   uint32_t qxor;
+  int xcd_w;  // work-list window, see xcd_work_item
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -146,40 +146,9 @@ void fwd_kernel(const FwdParams prm) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  // Block -> work item.  Blocks are dealt to the XCDs round-robin (block i
-  // runs on XCD i % 8), and each XCD should get an equal share of the work
-  // with its K/V tiles staying in its own L2.  When Hq is a multiple of 8,
-  // XCD x takes query heads [x*Hq/8, (x+1)*Hq/8) of every sequence (the heads
-  // that share a K/V head are adjacent, so they land together), which keeps
-  // the XCDs balanced even when packed sequences differ in length.
-  // Within an XCD the items go sequence by sequence, then by runs of gx
-  // adjacent heads that share a K/V head (gx = gcd(Hq/Hkv, Hq/8)), then
-  // heaviest query tile first, the run's heads innermost: the heads reading
-  // one K/V tile run at the same time and share it in L2.
-  // Otherwise XCD x takes the x-th contiguous slice of the (batch, head,
-  // query tile) list.
   const int nqt = (prm.Lq + BM - 1) / BM;
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   int b, h, qt;
-  if (Hq % kXcds == 0) {
-    const int hx = Hq / kXcds;
-    int gx = Hq / Hkv, m = hx;  // gx = gcd(group size, hx)
-    while (m != 0) { const int t = gx % m; gx = m; m = t; }
-    const int per_b = hx * nqt;
-    b = slot / per_b;
-    const int r = slot - b * per_b;
-    const int run = r / (nqt * gx);
-    const int r2 = r - run * (nqt * gx);
-    qt = r2 / gx;
-    h = xcd * hx + run * gx + (r2 - qt * gx);
-  } else {
-    const int N = nqt * B * Hq;
-    const int item = xcd * (N / kXcds) + min(xcd, N % kXcds) + slot;
-    const int bhi = item / nqt;
-    qt = item - bhi * nqt;
-    b = bhi / Hq;
-    h = bhi - b * Hq;
-  }
+  xcd_work_item(B, Hq, nqt, prm.xcd_w, b, h, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
   const int bh = b * Hq + h;
   const int kvh = h / (Hq / Hkv);
@@ -566,6 +535,8 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   // Rescale threshold of 8 (log2 units) expressed in raw score units.
   p.thr = 8.f / p.scale2;
   p.qxor = (s < 0.f) ? 0x80008000u : 0u;
+  // blocks resident per CU at this kernel's register use: 3 (D=64), 2, 1 (D=256)
+  p.xcd_w = xcd_window(a.B, a.Hq, a.Hkv, nqt, D == 64 ? 3 : D == 128 ? 2 : 1);
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)nblocks), dim3(kNT), 0, stream, p);
   return hipGetLastError();
 }

@@ -39,7 +39,6 @@ constexpr int kPT = kPW * 64;     // threads
 constexpr int kPR = 32;           // query rows per wave
 constexpr int kPBM = kPW * kPR;   // query rows per workgroup
 constexpr int kPBN = 64;          // keys per tile
-constexpr int kXcd = 8;
 
 struct Fp8Params {
   const uint8_t* Q;
@@ -53,6 +52,7 @@ struct Fp8Params {
   float thr;     // lazy-rescale slack in raw score units
   float oscale;  // v_descale / 256
   uint32_t qxor; // sign flip of q for a negative scale
+  int xcd_w;     // work-list window, see xcd_work_item
 };
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -92,28 +92,9 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
 
-  // Block -> (b, h, query tile): XCD x takes query heads [x*Hq/8, (x+1)*Hq/8)
-  // of every sequence when Hq is a multiple of 8, else a contiguous slice of
-  // the list; heaviest query tile first.
   const int nqt = (Lq + kPBM - 1) / kPBM;
-  const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
   int b, h, qt;
-  if (Hq % kXcd == 0) {
-    const int hx = Hq / kXcd;
-    const int per_b = hx * nqt;
-    b = slot / per_b;
-    const int r = slot - b * per_b;
-    const int hh = r / nqt;
-    qt = r - hh * nqt;
-    h = xcd * hx + hh;
-  } else {
-    const int N = nqt * B * Hq;
-    const int item = xcd * (N / kXcd) + min(xcd, N % kXcd) + slot;
-    const int bhi = item / nqt;
-    qt = item - bhi * nqt;
-    b = bhi / Hq;
-    h = bhi - b * Hq;
-  }
+  xcd_work_item(B, Hq, nqt, prm.xcd_w, b, h, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int kvh = h / (Hq / Hkv);
   const int shift = Lk - Lq;
@@ -317,6 +298,8 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
   p.oscale = a.v_descale / 256.f;
   p.qxor = sc < 0.f ? 0x80808080u : 0u;
   const int nqt = (a.Lq + kPBM - 1) / kPBM;
+  // blocks resident per CU at this kernel's register use: 4 (D=64), 3 (D=128)
+  p.xcd_w = xcd_window(a.B, a.Hq, a.Hkv, nqt, D == 64 ? 4 : 3);
   const dim3 grid((unsigned)((long)nqt * a.B * a.Hq));
   if (a.causal)
     hipLaunchKernelGGL((fwd_fp8_kernel<D, OT, true>), grid, dim3(kPT), 0, stream, p);
