@@ -47,8 +47,8 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_fa_amd", "csrc")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
@@ -220,7 +220,21 @@ PAGED_FORMATS = {"native": (False, False), "k8": (True, False), "kv8": (True, Tr
 PAGE_SIZE = 16
 
 
-def time_paged(fmt, dev, reps=10, warmup=3):
+def settle(run, seconds=0.25):
+    """Untimed: repeat run() for `seconds` of wall time so that the GPU clocks
+    have ramped up before a measurement (a few calls are not enough; the first
+    ~100 ms of work after idle run 10-20 % slow)."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            run()
+        torch.cuda.synchronize()
+
+
+def time_paged(fmt, dev, reps=10):
     """The decode workload in a paged cache of 16-slot pages (native, int8
     keys, or int8 keys and values): mean time of fa_decode_paged (split +
     combine, HIP events on the launch stream) and algorithmic GB/s."""
@@ -242,8 +256,7 @@ def time_paged(fmt, dev, reps=10, warmup=3):
     run = lambda: flash_attn_decode_paged(q, kp, vp, table, lens_d, k_scales=ks, v_scales=vs,
                                           softmax_scale=sc, num_splits=cfg.num_splits,
                                           workspace=ws, out=o, lse=lse)
-    for _ in range(warmup):
-        run()
+    settle(run)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     torch.cuda.synchronize()
@@ -268,7 +281,7 @@ def time_paged(fmt, dev, reps=10, warmup=3):
                          "traffic": traffic}}
 
 
-def time_bwd(dev, reps=10, warmup=3):
+def time_bwd(dev, reps=10):
     """fa_bwd (prep + dQ + dK/dV kernels) on the Llama-2-7B-shaped causal
     workload, fed by one untimed fa_fwd: mean time (HIP events on the launch
     stream) and algorithmic TFLOP/s (10*D per allowed pair per query head:
@@ -291,8 +304,7 @@ def time_bwd(dev, reps=10, warmup=3):
                      device=dev)
     run = lambda: flash_attn_bwd(q, k, v, o, lse, do, softmax_scale=sc, causal=cfg.causal, dq=dq,
                                  dk=dk, dv=dv, workspace=ws)
-    for _ in range(warmup):
-        run()
+    settle(run)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     torch.cuda.synchronize()
@@ -320,7 +332,7 @@ def time_bwd(dev, reps=10, warmup=3):
                                                                       "fa_common.hpp"]))}}
 
 
-def time_fp8(dev, reps=10, warmup=3):
+def time_fp8(dev, reps=10):
     """fa_fwd_fp8 on the Llama-2-7B-shaped causal workload with e4m3 Q, K, V:
     mean time (HIP events on the launch stream) and algorithmic TFLOP/s
     (4*D per allowed pair per query head) against the fp8 MFMA peak."""
@@ -338,8 +350,7 @@ def time_fp8(dev, reps=10, warmup=3):
     sc = float(np.float32(cfg.scale))
     run = lambda: flash_attn_fwd_fp8(q8, k8, vt8, q_descale=ds, k_descale=ds, v_descale=ds,
                                      softmax_scale=sc, causal=True, out=o, lse=lse)
-    for _ in range(warmup):
-        run()
+    settle(run)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     torch.cuda.synchronize()
@@ -366,7 +377,7 @@ def time_fp8(dev, reps=10, warmup=3):
             "kernel": "fwd_fp8_kernel<128, bf16_t, true>"}
 
 
-def time_masked(cfg, dev, reps=10, warmup=3):
+def time_masked(cfg, dev, reps=10):
     """Mean launch time (ms, HIP events on the launch stream) of one
     structured-mask workload, and its algorithmic TFLOP/s."""
     import numpy as np
@@ -387,8 +398,7 @@ def time_masked(cfg, dev, reps=10, warmup=3):
         lse = torch.empty((cfg.nseq, cfg.Hq, lmax), dtype=torch.float32, device=dev)
         run = lambda: flash_attn_fwd(q, k, v, softmax_scale=sc, causal=cfg.causal,
                                      window=cfg.window, out=o, lse=lse)
-    for _ in range(warmup):
-        run()
+    settle(run)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     torch.cuda.synchronize()
@@ -593,8 +603,7 @@ def main():
         for name, cfg in W.PREFILL.items():
             qq, kk, vv = (t.to(dev) for t in W.prefill_inputs(cfg))
             sc = float(np.float32(cfg.scale))
-            for _ in range(3):
-                flash_attn_fwd(qq, kk, vv, softmax_scale=sc, causal=cfg.causal)
+            settle(lambda: flash_attn_fwd(qq, kk, vv, softmax_scale=sc, causal=cfg.causal))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 20
             e0.record()
