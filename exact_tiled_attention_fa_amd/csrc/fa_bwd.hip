@@ -22,13 +22,15 @@
 //     from LDS, B = Q^T or dO^T held in registers), then dS^T in registers,
 //     then dQ^T += K^T dS^T (A = K^T by transpose reads of the same K tile,
 //     B = dS^T straight from the accumulator, rounded to 16 bits).
-//   * dkdv (key-major): a workgroup owns 128 keys (32 per wave, one per lane
-//     column) of one K/V head and streams tiles of 32 query rows of every
-//     query head of its group (Q, dO, lse, D) through LDS.  Per tile and wave:
-//     S = Q K^T and dP = dO V^T (A = Q or dO rows from LDS, B = K^T or V^T in
-//     registers), then P and dS, then dV^T += dO^T P and dK^T += Q^T dS (A by
-//     transpose reads of the dO and Q tiles).  The group's query heads add
-//     into the same accumulators, so GQA needs no reduction pass.
+//   * dkdv (key-major): a workgroup of 8 waves owns 128 keys of one K/V head
+//     (32 per pair of waves, one per lane column) and streams tiles of 32
+//     query rows of every query head of its group (Q, dO, lse, D) through
+//     LDS.  Per tile, one wave of a pair computes S = Q K^T (A = Q rows from
+//     LDS, B = K^T in registers), P and dV^T += dO^T P (A by transpose reads
+//     of the dO tile) and hands P to its partner through LDS; the partner
+//     computes dP = dO V^T, then dS and dK^T += Q^T dS.  Each wave so holds
+//     one accumulator and one operand.  The group's query heads add into the
+//     same accumulators, so GQA needs no reduction pass.
 // Masks (causal, sliding window, the key count) are those of the forward;
 // tiles a wave's rows cannot see are skipped, partly visible ones are masked.
 #include <type_traits>
@@ -331,31 +333,107 @@ void bwd_dq_kernel(const BwdParams p) {
 }
 
 // -------------------------------------------------------------------------
-// dK, dV: key-major.
+// dK, dV: key-major, waves in pairs.
 // -------------------------------------------------------------------------
+constexpr int kKW = 8;         // waves per dK/dV workgroup: 4 pairs x 32 keys
+constexpr int kKT = kKW * 64;  // threads per dK/dV workgroup
+
+// LDS-direct copy of one query tile of Q and of dO (ROWS x D each; rows past
+// `last` re-read `last`) by all the waves of a dK/dV workgroup: load i of
+// thread t moves chunk (i * 8 + wave) * 64 + lane of the list [Q chunks, dO
+// chunks], 16-byte chunks XOR-swizzled by row as in TileLoader.
+template <int D, int ROWS>
+struct PairTileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int QCH = ROWS * CPR;  // chunks per tile
+  static constexpr int NLOAD = 2 * QCH / kKT;
+  static_assert((2 * QCH) % kKT == 0 && QCH % 64 == 0, "tile shape");
+  uint32_t off[NLOAD];
+  int rr[NLOAD];
+  __device__ __forceinline__ void init(int wu, int lane, int stride) {
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      const int P = (i * kKW + wu) * 64 + lane;
+      const int c = P < QCH ? P : P - QCH;
+      const int r = c / CPR, pc = c % CPR;
+      rr[i] = r;
+      off[i] = 2u * (uint32_t)(r * stride + 8 * (pc ^ swz_b<D>(r)));
+    }
+  }
+  __device__ __forceinline__ void issue(const uint16_t* q, const uint16_t* g, int r0, int last,
+                                        int stride, int wu, uint16_t* dq, uint16_t* dg) const {
+    const long rb = (long)r0 * stride;
+    const bool whole = r0 + ROWS - 1 <= last;
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      const int c0 = (i * kKW + wu) * 64;  // wave-uniform first chunk
+      const bool isg = c0 >= QCH;
+      uint32_t o = off[i];
+      if (!whole) o -= 2u * (uint32_t)(((r0 + rr[i]) - min(r0 + rr[i], last)) * stride);
+      load_lds16_off((isg ? g : q) + rb, o, (isg ? dg : dq) + (isg ? c0 - QCH : c0) * 8);
+    }
+  }
+};
+
+// A workgroup owns 128 keys of one K/V head: 4 pairs of waves, 32 keys per
+// pair (one per lane column).  It streams tiles of 32 query rows of every
+// query head of the group (Q, dO, lse, D) through LDS.  Within a pair the
+// work of a tile is split so that each wave holds one 32 x D accumulator and
+// one operand, which keeps two waves per SIMD resident:
+//   * wave "P" holds K^T: S = Q K^T, P = exp2(S log2e - lse) on the visible
+//     entries, then dV^T += dO^T P; it also stores P (fp32, in its
+//     accumulator layout) in LDS for its partner;
+//   * wave "S" holds V^T: dP = dO V^T for the tile; one step later (after
+//     the barrier that also guards the copies) it reads P back at the same
+//     layout, forms dS = P (dP - D) and adds dK^T += Q^T dS.
+// The partner's lag keeps the previous tile's Q in LDS: three stages of Q /
+// dO tiles (current, previous, next) and two of the P exchange.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBT, 1)
+__global__ __launch_bounds__(kKT, 1)
 void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BQ = kTile;
   constexpr int TILE = BQ * D;
+  // Distinct arrays per stage: the compiler then sees that reading one stage
+  // does not alias the LDS-direct copy into another and adds no wait.
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sG0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sQ1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sG1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG2[TILE];
   __shared__ __attribute__((aligned(16))) float sL0[2 * BQ];  // lse2 then D of the tile's rows
   __shared__ __attribute__((aligned(16))) float sL1[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float sL2[2 * BQ];
+  // P exchange: [step parity][pair][4 x 64 lanes x 4 floats]
+  __shared__ __attribute__((aligned(16))) float sX[2][kKW / 2][16 * 64];
+  auto qst = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return sQ0; else if constexpr (i == 1) return sQ1; else return sQ2;
+  };
+  auto gst = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return sG0; else if constexpr (i == 1) return sG1; else return sG2;
+  };
+  auto lst = [&](auto I) -> float* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return sL0; else if constexpr (i == 1) return sL1; else return sL2;
+  };
 
   const int Hq = p.Hq, Hkv = p.Hkv, Lq = p.Lq, Lk = p.Lk;
   const int g = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
+  const int pair = wu >> 1;
+  // Role per wave, alternated so that each SIMD (wave w runs on SIMD w % 4)
+  // gets one wave of each kind: 1 = the dS / dK wave.
+  const bool sw = ((wu & 1) ^ ((wu >> 2) & 1)) != 0;
   // Key tiles ascending: under a causal mask the first see the most queries.
   int bkv, kt;
   xcd_item(p.B * Hkv, bkv, kt);
   const int b = bkv / Hkv, kvh = bkv - b * Hkv;
   const int shift = Lk - Lq;
-  const int k0 = kt * kBM, kw0 = k0 + kBR * w, key = kw0 + l32;
+  const int k0 = kt * kBM, kw0 = k0 + kBR * pair, key = kw0 + l32;
   const int k_last = min(k0 + kBM, Lk) - 1;
   const int kw_last = min(kw0 + kBR - 1, Lk - 1);
   const int wl = p.win_left, wr = p.win_right;
@@ -377,36 +455,40 @@ void bwd_dkdv_kernel(const BwdParams p) {
 
   const int kstride = Hkv * D;
   const int qstride = Hq * D;
-  // K^T and V^T operands: lane holds key `key` (clamped), 8 dims per k-step.
-  u32x4 kf[D / 16], vf[D / 16];
-  const long krow = ((long)b * Lk + min(key, Lk - 1)) * kstride + (long)kvh * D;
+  // This wave's operand: K^T (P wave) or V^T (dS wave); lane holds key `key`
+  // (clamped), 8 dims per k-step.
+  u32x4 kv[D / 16];
+  {
+    const long krow = ((long)b * Lk + min(key, Lk - 1)) * kstride + (long)kvh * D;
+    const uint16_t* src = sw ? p.V : p.K;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    kf[s] = load16(p.K + krow + 16 * s + 8 * hf);
-    vf[s] = load16(p.V + krow + 16 * s + 8 * hf);
+    for (int s = 0; s < D / 16; ++s) kv[s] = load16(src + krow + 16 * s + 8 * hf);
   }
 
   const int i_lo = qlo(k0), i_hi = qhi(k_last);
   const int s_first = i_lo / BQ;
   const int nsteps = (k0 < Lk && i_hi >= i_lo) ? i_hi / BQ - s_first + 1 : 0;
   const int wi_lo = qlo(kw0), wi_hi = qhi(kw_last);
-  const bool wave_live = kw0 < Lk && wi_hi >= wi_lo;
-  const int first_live = wave_live ? wi_lo / BQ - s_first : nsteps;
-  const int last_live = wave_live ? wi_hi / BQ - s_first : -1;
+  const bool pair_live = kw0 < Lk && wi_hi >= wi_lo;
+  const int first_live = pair_live ? wi_lo / BQ - s_first : nsteps;
+  const int last_live = pair_live ? wi_hi / BQ - s_first : -1;
   const int ntiles = g * nsteps;  // (query head of the group, query step) pairs
+  auto live = [&](int u) {
+    const int st = u % nsteps;
+    return st >= first_live && st <= last_live;
+  };
 
-  TileLoader<D, BQ> ldr;
+  PairTileLoader<D, BQ> ldr;
   ldr.init(wu, lane, qstride);
   int toff[D / 32][2];
   tr_offsets<D>(lane, toff);
 
   // lse2 / D copy: wave 0, lanes 0..15 (8 chunks of 4 rows each).
-  auto issue_tile = [&](int u, uint16_t* dq_tile, uint16_t* dg_tile, float* dl) {
+  auto issue_tile = [&](int u, uint16_t* dq_tile, uint16_t* dg_tile, float* dl) __attribute__((always_inline)) {
     const int hh = kvh * g + u / nsteps;
     const int q0 = (s_first + u % nsteps) * BQ;
     const long hbase = (long)b * Lq * qstride + (long)hh * D;
-    ldr.issue(p.Q + hbase, q0, Lq - 1, qstride, wu, dq_tile);
-    ldr.issue(p.dO + hbase, q0, Lq - 1, qstride, wu, dg_tile);
+    ldr.issue(p.Q + hbase, p.dO + hbase, q0, Lq - 1, qstride, wu, dq_tile, dg_tile);
     if (wu == 0 && lane < 16) {
       const long sb = ((long)b * Hq + hh) * p.Lqp + q0;  // rows q0..q0+31 < Lqp
       const float* src = (lane < 8 ? p.lse2 : p.Dd) + sb + 4 * (lane & 7);
@@ -414,89 +496,133 @@ void bwd_dkdv_kernel(const BwdParams p) {
     }
   };
 
-  f32x16 dv[D / 32], dk[D / 32];
+  f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    dv[i] = (f32x16){};
-    dk[i] = (f32x16){};
-  }
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  f32x16 dp = (f32x16){};  // dS wave: dP of the previous step's tile
   const float scale2 = p.scale2;
   const uint32_t qxor = p.qxor;
 
-  auto compute = [&](int u, const uint16_t* sQ, const uint16_t* sG, const float* sL) {
-    const int st = u % nsteps;
-    if (st < first_live || st > last_live) return;
-    const int q0 = (s_first + st) * BQ;
-    f32x16 s = (f32x16){}, dp = (f32x16){};
+  // P wave, tile u: S, P (stored for the partner), dV^T += dO^T P.
+  auto p_tile = [&](int u, const uint16_t* sQ, const uint16_t* sG, const float* sL) __attribute__((always_inline)) {
+    const int q0 = (s_first + u % nsteps) * BQ;
+    f32x16 s = (f32x16){};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s = Ops<T>::mfma32(ld_row_chunk<D>(sQ, l32, 2 * kk + hf) ^ qxor, kf[kk], s);
-      dp = Ops<T>::mfma32(ld_row_chunk<D>(sG, l32, 2 * kk + hf), vf[kk], dp);
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+      s = Ops<T>::mfma32(ld_row_chunk<D>(sQ, l32, 2 * kk + hf) ^ qxor, kv[kk], s);
     // element r: query q0 + 8(r/4) + 4hf + r%4, key `key`
     const int qlast = min(q0 + BQ, Lq) - 1;
     const bool whole = q0 + BQ <= Lq && kw0 >= kmin(qlast) && kw0 + kBR - 1 <= kmax(q0) &&
                        kw0 + kBR <= Lk;
-    uint32_t pk[8], dsk[8];
+    float* xs = &sX[u & 1][pair][0];
+    uint32_t pk[8];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 8 * gq + 4 * hf);
-      const f32x4 D4 = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * gq + 4 * hf);
-      float pr[4], ds[4];
+      f32x4 pr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 4 * gq + i;
         const int qi = q0 + 8 * gq + 4 * hf + i;
         const bool vis = whole || (qi < Lq && key >= kmin(qi) && key <= kmax(qi));
-        const float e = exp2_fast(__builtin_fmaf(s[r], scale2, -L4[i]));
+        const float e = exp2_fast(__builtin_fmaf(s[4 * gq + i], scale2, -L4[i]));
         pr[i] = vis ? e : 0.f;
-        ds[i] = vis ? e * (dp[r] - D4[i]) : 0.f;
       }
+      *reinterpret_cast<f32x4*>(xs + 4 * (gq * 64 + lane)) = pr;
       pk[2 * gq] = Ops<T>::pack2(pr[0], pr[1]);
       pk[2 * gq + 1] = Ops<T>::pack2(pr[2], pr[3]);
-      dsk[2 * gq] = Ops<T>::pack2(ds[0], ds[1]);
-      dsk[2 * gq + 1] = Ops<T>::pack2(ds[2], ds[3]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per k-step
+    // dV^T += dO^T P, 16 query rows per k-step
 #pragma unroll
     for (int ts = 0; ts < BQ / 16; ++ts) {
       const u32x4 pb = {pk[4 * ts], pk[4 * ts + 1], pk[4 * ts + 2], pk[4 * ts + 3]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma_tr<T, D>(sG, toff, db, ts, pb, acc[db]);
+    }
+  };
+  // dS wave, tile u: dP = dO V^T.
+  auto dp_tile = [&](const uint16_t* sG) __attribute__((always_inline)) {
+    dp = (f32x16){};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      dp = Ops<T>::mfma32(ld_row_chunk<D>(sG, l32, 2 * kk + hf), kv[kk], dp);
+  };
+  // dS wave, tile u (one step later): dS = P (dP - D), dK^T += Q^T dS.
+  // Entries the rows may not see have P = 0 and give dS = 0 (the test on P
+  // also keeps the unset D of padding rows out).
+  auto ds_tile = [&](int u, const uint16_t* sQ, const float* sL) __attribute__((always_inline)) {
+    const float* xs = &sX[u & 1][pair][0];
+    uint32_t dsk[8];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4 D4 = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * gq + 4 * hf);
+      const f32x4 pr = *reinterpret_cast<const f32x4*>(xs + 4 * (gq * 64 + lane));
+      float ds[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds[i] = pr[i] != 0.f ? pr[i] * (dp[4 * gq + i] - D4[i]) : 0.f;
+      dsk[2 * gq] = Ops<T>::pack2(ds[0], ds[1]);
+      dsk[2 * gq + 1] = Ops<T>::pack2(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int ts = 0; ts < BQ / 16; ++ts) {
       const u32x4 db_ = {dsk[4 * ts], dsk[4 * ts + 1], dsk[4 * ts + 2], dsk[4 * ts + 3]};
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dv[db] = mfma_tr<T, D>(sG, toff, db, ts, pb, dv[db]);
-        dk[db] = mfma_tr<T, D>(sQ, toff, db, ts, db_, dk[db]);
-      }
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma_tr<T, D>(sQ, toff, db, ts, db_, acc[db]);
+    }
+  };
+
+  // Step u (0 .. ntiles): tile u sits in stage u % 3, tile u - 1 in the stage
+  // before.  The barrier makes tile u's copies visible and ends every wave's
+  // step u - 1 (its reads of the stage refilled next, its P stores); then the
+  // copies of tile u + 1 are issued and the pair works on tiles u and u - 1.
+  // The two kinds of wave run separate loops (so their registers are not
+  // allocated side by side) with the same barriers.
+  auto step = [&](int u, auto I, auto role) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    using Inext = std::integral_constant<int, (i + 1) % 3>;
+    using Iprev = std::integral_constant<int, (i + 2) % 3>;
+    copies_done_barrier();
+    if (u + 1 < ntiles) issue_tile(u + 1, qst(Inext{}), gst(Inext{}), lst(Inext{}));
+    if constexpr (!decltype(role)::value) {
+      if (u < ntiles && live(u)) p_tile(u, qst(I), gst(I), lst(I));
+    } else {
+      if (u >= 1 && live(u - 1)) ds_tile(u - 1, qst(Iprev{}), lst(Iprev{}));
+      if (u < ntiles && live(u)) dp_tile(gst(I));
+    }
+  };
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    for (int u = 0;; u += 3) {
+      step(u, S0{}, role);
+      if (u + 1 > ntiles) break;
+      step(u + 1, S1{}, role);
+      if (u + 2 > ntiles) break;
+      step(u + 2, S2{}, role);
+      if (u + 3 > ntiles) break;
     }
   };
 
   if (ntiles > 0) {
     issue_tile(0, sQ0, sG0, sL0);
-    for (int u = 0; u < ntiles; u += 2) {
-      copies_done_barrier();
-      if (u + 1 < ntiles) issue_tile(u + 1, sQ1, sG1, sL1);
-      compute(u, sQ0, sG0, sL0);
-      if (u + 1 >= ntiles) break;
-      copies_done_barrier();
-      if (u + 2 < ntiles) issue_tile(u + 2, sQ0, sG0, sL0);
-      compute(u + 1, sQ1, sG1, sL1);
-    }
+    if (sw)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   }
 
   if (key < Lk) {
     const long orow = ((long)b * Lk + key) * kstride + (long)kvh * D;
-    const float sc = p.scale;
+    uint16_t* out = (sw ? p.dK : p.dV) + orow;
+    const float sc = sw ? p.scale : 1.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const int d = 32 * db + 8 * gg + 4 * hf;
-        *reinterpret_cast<u32x2*>(p.dK + orow + d) =
-            (u32x2){Ops<T>::pack2(dk[db][4 * gg] * sc, dk[db][4 * gg + 1] * sc),
-                    Ops<T>::pack2(dk[db][4 * gg + 2] * sc, dk[db][4 * gg + 3] * sc)};
-        *reinterpret_cast<u32x2*>(p.dV + orow + d) =
-            (u32x2){Ops<T>::pack2(dv[db][4 * gg], dv[db][4 * gg + 1]),
-                    Ops<T>::pack2(dv[db][4 * gg + 2], dv[db][4 * gg + 3])};
+        *reinterpret_cast<u32x2*>(out + d) =
+            (u32x2){Ops<T>::pack2(acc[db][4 * gg] * sc, acc[db][4 * gg + 1] * sc),
+                    Ops<T>::pack2(acc[db][4 * gg + 2] * sc, acc[db][4 * gg + 3] * sc)};
       }
   }
 }
@@ -538,11 +664,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (a.causal) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), gq, dim3(kBT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), gk, dim3(kBT), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), gk, dim3(kKT), 0, stream, p);
   } else {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), gq, dim3(kBT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), gk, dim3(kBT), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), gk, dim3(kKT), 0, stream, p);
   }
   return hipGetLastError();
 }
