@@ -332,6 +332,54 @@ def time_bwd(dev, reps=10):
                                                                       "fa_common.hpp"]))}}
 
 
+def time_bwd_varlen(dev, reps=10):
+    """fa_bwd_ex on the varlen16 workload (16 causal sequences packed back to
+    back, lengths U[256, 4096], Hq=32, Hkv=8, D=128, bf16), fed by one untimed
+    packed forward: mean time (HIP events) and algorithmic TFLOP/s (10*D per
+    allowed pair per query head)."""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import _abi
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import flash_attn_varlen, flash_attn_varlen_bwd
+
+    cfg = W.MASKED["varlen16"]
+    q, k, v, cu = W.masked_inputs(cfg)
+    lens = cfg.lengths()
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(cfg.seed + 2)).to(cfg.dtype)
+    q, k, v, cu, do = (t.to(dev) for t in (q, k, v, cu, do))
+    L = max(lens)
+    sc = float(np.float32(cfg.scale))
+    o, lse = flash_attn_varlen(q, k, v, cu, cu, L, L, softmax_scale=sc, causal=cfg.causal,
+                               window=cfg.window)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((_abi.fa_bwd_workspace_size(cfg.nseq, cfg.Hq, L),), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: flash_attn_varlen_bwd(q, k, v, o, lse, do, cu, cu, L, L, softmax_scale=sc,
+                                        causal=cfg.causal, window=cfg.window, dq=dq, dk=dk, dv=dv,
+                                        workspace=ws)
+    settle(run)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    mean = float(np.mean(ms))
+    flops = cfg.flops() // 4 * 10
+    tf = flops / (mean * 1e-3) / 1e12
+    return {"workload": "varlen16 causal backward: 16 packed sequences U[256,4096], Hq=32 Hkv=8 "
+                        "D=128 bf16 (dQ, dK, dV)",
+            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
+                   "min": round(float(np.min(ms)), 5)},
+            "alg_flops_per_launch": flops, "value": round(tf, 3), "unit": "TFLOP/s",
+            "frac_mfma": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}
+
+
 def time_fp8(dev, reps=10):
     """fa_fwd_fp8 on the Llama-2-7B-shaped causal workload with e4m3 Q, K, V:
     mean time (HIP events on the launch stream) and algorithmic TFLOP/s
@@ -587,6 +635,7 @@ def main():
     if do_pf and not args.no_bwd:
         print("# backward workload", file=sys.stderr, flush=True)
         out["backward"] = time_bwd(dev)
+        out["backward"]["varlen16"] = time_bwd_varlen(dev)
     if do_pf and not args.no_masks:
         print("# structured-mask workloads", file=sys.stderr, flush=True)
         out["masks"] = {name: time_masked(cfg, dev) for name, cfg in masks.items()}

@@ -47,6 +47,8 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (_Z, [_I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P,
                     _Z, _I, _P]),
+    "fa_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                       _F, _I, _I, _I, _P, _Z, _I, _P]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_info": (ctypes.c_char_p, []),
 }
@@ -126,6 +128,14 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, caus
            window_right, workspace, workspace_bytes, dtype, stream) -> int:
     return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal,
                          window_left, window_right, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Lq, Lk,
+              total_q, total_k, D, scale, causal, window_left, window_right, workspace,
+              workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, Hq,
+                            Hkv, Lq, Lk, total_q, total_k, D, scale, causal, window_left,
+                            window_right, workspace, workspace_bytes, dtype, stream)
 
 
 def fa_last_error() -> str:

@@ -198,6 +198,53 @@ def flash_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
     return out, lse
 
 
+def flash_attn_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                          lse: torch.Tensor, dout: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                          cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
+                          softmax_scale=None, causal: bool = False, window=(-1, -1), dq=None,
+                          dk=None, dv=None, workspace=None):
+    """Gradients of flash_attn_varlen for packed sequences: q, out, dout
+    [total_q,Hq,D], k, v [total_k,Hkv,D], lse [Hq,total_q] float32 as the
+    forward wrote it.  Returns (dq, dk, dv) in q's dtype.  D in {64, 128}."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse"), (dout, "dout"),
+                 (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        _check_dev(t, n)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or out.shape != q.shape:
+        raise ValueError("expected q, out [total_q,Hq,D] and k, v [total_k,Hkv,D]")
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout must share dtype float16 or bfloat16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if Dk != D:
+        raise ValueError("head_dim mismatch between q and k")
+    if lse.dtype != torch.float32 or lse.shape != (Hq, total_q):
+        raise ValueError("lse must be float32 [Hq, total_q]")
+    B = cu_seqlens_q.shape[0] - 1
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        n = _abi.fa_bwd_workspace_size(B, Hq, int(max_seqlen_q))
+        workspace = torch.empty((max(n, 16),), dtype=torch.uint8, device=q.device)
+    st = _abi.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                        dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq,
+                        Hkv, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, D, scale,
+                        1 if causal else 0, int(window[0]), int(window[1]), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), _DTYPES[q.dtype],
+                        _stream_handle(q.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_bwd_ex")
+    return dq, dk, dv
+
+
 def decode_workspace(B: int, Hq: int, D: int, num_splits: int, device) -> torch.Tensor:
     """A byte tensor large enough for fa_decode's workspace."""
     n = _abi.fa_decode_workspace_size(B, Hq, D, num_splits)

@@ -284,10 +284,12 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Lq) {
   return fa::bwd_workspace_bytes(B, Hq, Lq);
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq,
-                 int Lk, int D, float scale, int causal, int window_left, int window_right,
-                 void* workspace, size_t workspace_bytes, fa_dtype dtype, hipStream_t stream) {
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int B, int Hq, int Hkv, int Lq, int Lk, int total_q,
+                    int total_k, int D, float scale, int causal, int window_left,
+                    int window_right, void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                    hipStream_t stream) {
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(k, "k"));
   FA_TRY(check_ptr(v, "v"));
@@ -298,6 +300,15 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   FA_TRY(check_ptr(dk, "dk"));
   FA_TRY(check_ptr(dv, "dv"));
   FA_TRY(check_ptr(workspace, "workspace"));
+  const bool packed = cu_seqlens_q != nullptr || cu_seqlens_k != nullptr;
+  if (packed) {
+    if (!cu_seqlens_q || !cu_seqlens_k)
+      return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");
+    if (((uintptr_t)cu_seqlens_q & 3u) || ((uintptr_t)cu_seqlens_k & 3u))
+      return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens arrays are not 4-byte aligned");
+    if (total_q < 1 || total_k < 1)
+      return fail(FA_ERR_INVALID_ARGUMENT, "total_q=%d and total_k=%d must be >= 1", total_q, total_k);
+  }
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || D < 1)
     return fail(FA_ERR_INVALID_ARGUMENT,
                 "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d)", B, Hq, Hkv, Lq, Lk, D);
@@ -310,12 +321,15 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     return fail(FA_ERR_UNSUPPORTED, "backward head_dim %d not in {64, 128}", D);
   if ((long long)Hq * D >= (1LL << 25) || (long long)Hkv * D >= (1LL << 25))
     return fail(FA_ERR_INVALID_ARGUMENT, "Hq * D and Hkv * D must be < 2^25");
-  if ((long long)B * Lq * Hq > 0x7fffffffLL || (long long)B * Lk * Hkv > 0x7fffffffLL)
-    return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
+  const long long rows_q = packed ? (long long)total_q : (long long)B * Lq;
+  const long long rows_k = packed ? (long long)total_k : (long long)B * Lk;
+  if (rows_q * Hq > 0x7fffffffLL || rows_k * Hkv > 0x7fffffffLL ||
+      (long long)B * Lq * Hq > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H (rows * heads) exceeds 2^31-1");
   if (((long long)Lq + 127) / 128 * B * Hq > 0x7fffffffLL ||
       ((long long)Lk + 127) / 128 * B * Hkv > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (L/128 * B * H > 2^31-1)");
-  const long long span = (long long)B * Lq + (long long)B * Lk;
+  const long long span = rows_q + rows_k;
   const bool windowed = window_left >= 0 || window_right >= 0;
   if (windowed && span > (1LL << 30))
     return fail(FA_ERR_INVALID_ARGUMENT, "windowed attention needs query + key rows <= 2^30");
@@ -328,9 +342,22 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                 (window_left < 0 || window_left >= span) ? -1 : window_left,
                 (window_right < 0 || window_right >= span) ? -1 : window_right, workspace,
                 dtype == FA_BF16 ? 1 : 0};
+  a.cu_q = packed ? cu_seqlens_q : nullptr;
+  a.cu_k = packed ? cu_seqlens_k : nullptr;
+  a.total_q = packed ? total_q : 0;
+  a.total_k = packed ? total_k : 0;
   hipError_t e = fa::launch_bwd(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq,
+                 int Lk, int D, float scale, int causal, int window_left, int window_right,
+                 void* workspace, size_t workspace_bytes, fa_dtype dtype, hipStream_t stream) {
+  return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, 0, 0,
+                   D, scale, causal, window_left, window_right, workspace, workspace_bytes, dtype,
+                   stream);
 }
 
 const char* fa_last_error(void) { return g_err; }
@@ -340,9 +367,10 @@ const char* fa_info(void) {
          "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), 32-key tiles, "
          "mfma_f32_32x32x16, LDS-direct K/V with transpose reads, causal/window tile "
          "skip, block-diagonal packing, GQA; "
+         "bwd: dQ query-major, dK/dV key-major in pairs of waves, dense and packed; "
          "decode: split-KV, 4 wave64 per (chunk, kv head, 16 heads, sequence), 16-key steps, "
          "mfma_f32_16x16x32 + 16x16x16, logsumexp combine, paged and int8 KV caches; "
-         "version=0.3.0";
+         "version=0.4.0";
 }
 
 }  // extern "C"

@@ -59,7 +59,10 @@ struct BwdParams {
   uint16_t* dV;
   float* lse2;  // workspace [B, Hq, Lqp]: lse * log2(e), +inf for rows with no key
   float* Dd;    // workspace [B, Hq, Lqp]: rowsum(dO * O)
-  int B, Hq, Hkv, Lq, Lk, Lqp;
+  const int* cu_q;  // packed sequences: offsets [B + 1] into the rows, or nullptr
+  const int* cu_k;
+  int total_q, total_k;  // packed row counts
+  int B, Hq, Hkv, Lq, Lk, Lqp;  // packed: Lq, Lk are the longest lengths
   int win_left, win_right;
   float scale2;  // |scale| * log2(e), >= 1e-30
   float scale;   // signed scale (factor of dQ and dK)
@@ -72,6 +75,23 @@ template <int D> __device__ __forceinline__ int swz_b(int r) {
   return D >= 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
+// Rows of sequence b: queries qs .. qs+Lq-1 and keys ks .. ks+Lk-1.  Packed
+// offsets are clamped into the tensors and the lengths to the longest ones
+// the grid and the workspace are sized for, so that inconsistent offsets give
+// wrong results but no out-of-bounds access.
+struct SeqRows {
+  int qs, Lq, ks, Lk;
+};
+__device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b) {
+  if (!p.cu_q) return {b * p.Lq, p.Lq, b * p.Lk, p.Lk};
+  SeqRows r;
+  r.qs = min(max(p.cu_q[b], 0), p.total_q);
+  r.Lq = min(min(max(p.cu_q[b + 1], r.qs), p.total_q) - r.qs, p.Lq);
+  r.ks = min(max(p.cu_k[b], 0), p.total_k);
+  r.Lk = min(min(max(p.cu_k[b + 1], r.ks), p.total_k) - r.ks, p.Lk);
+  return r;
+}
+
 // Per-row statistics: D_i = dO_i . O_i and lse_i * log2(e).  CPR lanes (one
 // 16-byte chunk each) per (row, head); rows in memory order [B, Lq, Hq].
 template <typename T, int D>
@@ -79,14 +99,24 @@ __global__ __launch_bounds__(256)
 void bwd_prep_kernel(const BwdParams p) {
   constexpr int CPR = D / 8;
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gid / CPR;  // (b * Lq + i) * Hq + h
+  const long row = gid / CPR;  // (b * Lq + i) * Hq + h; packed: Lq is the longest length
   const int c = (int)(gid % CPR);
   const long nrows = (long)p.B * p.Lq * p.Hq;
-  float acc = 0.f;
-  const bool valid = row < nrows;
+  const int h = (int)(row % p.Hq);
+  const long bi = row / p.Hq;
+  const int i = (int)(bi % p.Lq);
+  const int b = (int)(bi / p.Lq);
+  bool valid = row < nrows;
+  SeqRows sr{0, 0, 0, 0};
   if (valid) {
-    const u32x4 o = load16(p.O + row * D + 8 * c);
-    const u32x4 g = load16(p.dO + row * D + 8 * c);
+    sr = seq_rows(p, b);
+    valid = i < sr.Lq;
+  }
+  const long mrow = (long)(sr.qs + i) * p.Hq + h;  // row of O / dO in memory
+  float acc = 0.f;
+  if (valid) {
+    const u32x4 o = load16(p.O + mrow * D + 8 * c);
+    const u32x4 g = load16(p.dO + mrow * D + 8 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       acc += Ops<T>::lo(o[e]) * Ops<T>::lo(g[e]) + Ops<T>::hi(o[e]) * Ops<T>::hi(g[e]);
@@ -94,32 +124,44 @@ void bwd_prep_kernel(const BwdParams p) {
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (valid && c == 0) {
-    const int h = (int)(row % p.Hq);
-    const long bi = row / p.Hq;
-    const int i = (int)(bi % p.Lq);
-    const int b = (int)(bi / p.Lq);
     const long oi = ((long)b * p.Hq + h) * p.Lqp + i;
-    const float l = p.LSE[((long)b * p.Hq + h) * p.Lq + i];
+    // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
+    const long li = p.cu_q ? (long)h * p.total_q + sr.qs + i : ((long)b * p.Hq + h) * p.Lq + i;
+    const float l = p.LSE[li];
     p.Dd[oi] = acc;
     p.lse2[oi] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
-// Block -> (head row, tile).  Blocks start in index order, so tile-major
-// order (tile 0 of every head, then tile 1, ...) puts the heaviest tiles first
-// and the lightest in the tail.  Block i runs on XCD i % 8; when the heads
-// split evenly over the 8 XCDs, XCD x takes the x-th contiguous slice of
-// heads and walks it tile-major, so the tiles it streams stay in its own L2.
-__device__ __forceinline__ void xcd_item(int rows, int& row, int& tile) {
-  const int i = (int)blockIdx.x;
-  if (rows % 8 == 0) {
-    const int per = rows / 8, xcd = i % 8, slot = i / 8;
+// Block -> (sequence b, head h, tile rank).  Blocks start in index order,
+// so tile-major order (rank 0 of every head, then rank 1, ...) puts the
+// heaviest tiles first and the lightest in the tail.  Block i runs on XCD
+// i % 8.  When H is a multiple of 8, XCD x takes heads [x H/8, (x+1) H/8) of
+// every sequence (balanced even when packed sequences differ in length) and
+// walks them tile-major, so the tiles it streams stay in its own L2; else,
+// when B*H is, it takes the x-th contiguous slice of the (b, head) rows;
+// else the whole grid is walked tile-major.
+__device__ __forceinline__ void bwd_item(int B, int H, int& b, int& h, int& tile) {
+  const int i = (int)blockIdx.x, xcd = i % 8, slot = i / 8;
+  const int rows = B * H;
+  int row;
+  if (H % 8 == 0) {
+    const int hx = H / 8, per = B * hx;
+    tile = slot / per;
+    const int r = slot - tile * per;
+    b = r / hx;
+    h = xcd * hx + (r - b * hx);
+    return;
+  } else if (rows % 8 == 0) {
+    const int per = rows / 8;
     tile = slot / per;
     row = xcd * per + (slot - tile * per);
   } else {
     tile = i / rows;
     row = i - tile * rows;
   }
+  b = row / H;
+  h = row - b * H;
 }
 
 // LDS-direct copy of `rows` x D 16-bit elements (rows r0 .. r0+rows-1 of a
@@ -207,18 +249,21 @@ void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
 
-  const int Hq = p.Hq, Lq = p.Lq, Lk = p.Lk;
+  const int Hq = p.Hq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int nqt = (Lq + kBM - 1) / kBM;
-  int bh, tt;
-  xcd_item(p.B * Hq, bh, tt);
-  const int b = bh / Hq, h = bh - b * Hq;
+  const int nqt = (p.Lq + kBM - 1) / kBM;
+  int b, h, tt;
+  bwd_item(p.B, Hq, b, h, tt);
   const int qt = CAUSAL ? nqt - 1 - tt : tt;  // heaviest (last, under a causal mask) first
+  const SeqRows sr = seq_rows(p, b);
+  const int Lq = sr.Lq, Lk = sr.Lk;
+  const int q0 = qt * kBM;
+  if (q0 >= Lq) return;  // past this sequence's rows (whole workgroup)
   const int kvh = h / (Hq / p.Hkv);
   const int shift = Lk - Lq;
-  const int q0 = qt * kBM, qw0 = q0 + kBR * w, qrow = qw0 + l32;
+  const int qw0 = q0 + kBR * w, qrow = qw0 + l32;
   const int wl = p.win_left, wr = p.win_right;
   auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
   auto kmax = [&](int i) {
@@ -229,12 +274,12 @@ void bwd_dq_kernel(const BwdParams p) {
   };
   const long qstride = (long)Hq * D;
   const int kstride = p.Hkv * D;
-  const uint16_t* Kb = p.K + (long)b * Lk * kstride + (long)kvh * D;
-  const uint16_t* Vb = p.V + (long)b * Lk * kstride + (long)kvh * D;
+  const uint16_t* Kb = p.K + (long)sr.ks * kstride + (long)kvh * D;
+  const uint16_t* Vb = p.V + (long)sr.ks * kstride + (long)kvh * D;
 
   // Q^T and dO^T operands: lane holds query qrow, 8 dims per 16-dim k-step.
   u32x4 qf[D / 16], df[D / 16];
-  const long rowbase = ((long)b * Lq + min(qrow, Lq - 1)) * qstride + (long)h * D;
+  const long rowbase = ((long)sr.qs + min(qrow, Lq - 1)) * qstride + (long)h * D;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     qf[s] = load16(p.Q + rowbase + 16 * s + 8 * hf) ^ p.qxor;
@@ -319,7 +364,7 @@ void bwd_dq_kernel(const BwdParams p) {
   }
 
   if (qrow < Lq) {
-    uint16_t* out = p.dQ + ((long)b * Lq + qrow) * qstride + (long)h * D;
+    uint16_t* out = p.dQ + ((long)sr.qs + qrow) * qstride + (long)h * D;
     const float sc = p.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -419,7 +464,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
     if constexpr (i == 0) return sL0; else if constexpr (i == 1) return sL1; else return sL2;
   };
 
-  const int Hq = p.Hq, Hkv = p.Hkv, Lq = p.Lq, Lk = p.Lk;
+  const int Hq = p.Hq, Hkv = p.Hkv;
   const int g = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -429,11 +474,14 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // gets one wave of each kind: 1 = the dS / dK wave.
   const bool sw = ((wu & 1) ^ ((wu >> 2) & 1)) != 0;
   // Key tiles ascending: under a causal mask the first see the most queries.
-  int bkv, kt;
-  xcd_item(p.B * Hkv, bkv, kt);
-  const int b = bkv / Hkv, kvh = bkv - b * Hkv;
+  int b, kvh, kt;
+  bwd_item(p.B, Hkv, b, kvh, kt);
+  const SeqRows sr = seq_rows(p, b);
+  const int Lq = sr.Lq, Lk = sr.Lk;
+  const int k0 = kt * kBM;
+  if (k0 >= Lk) return;  // past this sequence's keys (whole workgroup)
   const int shift = Lk - Lq;
-  const int k0 = kt * kBM, kw0 = k0 + kBR * pair, key = kw0 + l32;
+  const int kw0 = k0 + kBR * pair, key = kw0 + l32;
   const int k_last = min(k0 + kBM, Lk) - 1;
   const int kw_last = min(kw0 + kBR - 1, Lk - 1);
   const int wl = p.win_left, wr = p.win_right;
@@ -459,7 +507,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // (clamped), 8 dims per k-step.
   u32x4 kv[D / 16];
   {
-    const long krow = ((long)b * Lk + min(key, Lk - 1)) * kstride + (long)kvh * D;
+    const long krow = ((long)sr.ks + min(key, Lk - 1)) * kstride + (long)kvh * D;
     const uint16_t* src = sw ? p.V : p.K;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) kv[s] = load16(src + krow + 16 * s + 8 * hf);
@@ -487,7 +535,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   auto issue_tile = [&](int u, uint16_t* dq_tile, uint16_t* dg_tile, float* dl) __attribute__((always_inline)) {
     const int hh = kvh * g + u / nsteps;
     const int q0 = (s_first + u % nsteps) * BQ;
-    const long hbase = (long)b * Lq * qstride + (long)hh * D;
+    const long hbase = (long)sr.qs * qstride + (long)hh * D;
     ldr.issue(p.Q + hbase, p.dO + hbase, q0, Lq - 1, qstride, wu, dq_tile, dg_tile);
     if (wu == 0 && lane < 16) {
       const long sb = ((long)b * Hq + hh) * p.Lqp + q0;  // rows q0..q0+31 < Lqp
@@ -612,7 +660,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   }
 
   if (key < Lk) {
-    const long orow = ((long)b * Lk + key) * kstride + (long)kvh * D;
+    const long orow = ((long)sr.ks + key) * kstride + (long)kvh * D;
     uint16_t* out = (sw ? p.dK : p.dV) + orow;
     const float sc = sw ? p.scale : 1.f;
 #pragma unroll
@@ -644,6 +692,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.Lq = a.Lq;
   p.Lk = a.Lk;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
   p.Lqp = bwd_padded_rows(a.Lq);
   p.lse2 = (float*)a.workspace;
   p.Dd = p.lse2 + (size_t)a.B * a.Hq * p.Lqp;

@@ -83,6 +83,9 @@ struct BwdArgs {
   int win_left, win_right;
   void* workspace;
   int bf16;
+  const int* cu_q = nullptr;  // packed sequences (device), or nullptr
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 struct Fp8Args {

@@ -261,6 +261,30 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int Lk, int D, float scale, int causal, int window_left, int window_right,
                  void* workspace, size_t workspace_bytes, fa_dtype dtype, hipStream_t stream);
 
+/*
+ * fa_bwd_ex -- fa_bwd for the structured masks of fa_fwd_ex: also for several
+ * sequences packed back to back (block-diagonal), the backward of fa_fwd_ex
+ * with the same offsets.
+ *
+ *   cu_seqlens_q, cu_seqlens_k, total_q, total_k
+ *               as in fa_fwd_ex: NULL for a dense batch (then exactly
+ *               fa_bwd); otherwise q, o, dout, dq are [total_q, Hq, D], k, v,
+ *               dk, dv are [total_k, Hkv, D], lse is [Hq, total_q], and Lq /
+ *               Lk must be at least the longest query / key sequence.  Each
+ *               sequence's dk, dv rows are written (zero for keys no query of
+ *               the sequence sees).  Offsets are clamped on the device and
+ *               lengths past Lq / Lk are cut to them: inconsistent offsets
+ *               give wrong results but no out-of-bounds access.
+ *   workspace   fa_bwd_workspace_size(B, Hq, Lq) bytes, Lq the longest.
+ *   other arguments as in fa_bwd, which is fa_bwd_ex with NULL offsets.
+ */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int B, int Hq, int Hkv, int Lq, int Lk, int total_q,
+                    int total_k, int D, float scale, int causal, int window_left,
+                    int window_right, void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                    hipStream_t stream);
+
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

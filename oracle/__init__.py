@@ -21,9 +21,10 @@ Contents
 ``attention.decode_paged_ref``
     Decode against a paged KV cache (page table per sequence), optionally
     with int8 keys and/or values carrying one scale per cached row.
-``backward.attention_bwd_ref``
+``backward.attention_bwd_ref`` / ``backward.varlen_bwd_ref``
     The gradients of the definition with respect to Q, K and V given dO
-    (the chain rule through scores, row softmax and weighted sum), float64.
+    (the chain rule through scores, row softmax and weighted sum), float64;
+    the second for sequences packed back to back as in ``varlen_ref``.
 ``fp8.attention_fp8_ref`` / ``fp8.e4m3_decode``
     The forward on e4m3-coded Q, K and V (transposed) with per-tensor
     descales: exact decoding of the codes, then ``attention_ref``.
@@ -40,13 +41,14 @@ than itself: a 40-digit ``decimal`` brute force, PyTorch's fp64 CPU
 
 from .attention import (attention_ref, causal_allowed, decode_paged_ref, decode_ref, key_bounds,
                         varlen_ref)
-from .backward import attention_bwd_ref
+from .backward import attention_bwd_ref, varlen_bwd_ref
 from .fp8 import attention_fp8_ref, e4m3_decode
 from .online import online_attention_ref, split_combine_ref
 
 __all__ = [
     "attention_ref",
     "attention_bwd_ref",
+    "varlen_bwd_ref",
     "attention_fp8_ref",
     "e4m3_decode",
     "decode_ref",

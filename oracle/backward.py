@@ -32,7 +32,11 @@ of the forward oracle and by PyTorch autograd.
 
 Implementation notes: one (batch, K/V head) at a time, its query heads in
 turn, query rows in blocks of ``row_block``; P is recomputed from the
-definition (the kernel's saved lse is not an input here).
+definition (the kernel's saved lse is not an input here).  For sequences
+packed back to back (``varlen_bwd_ref``) every sequence is its own batch
+entry: the forward it differentiates (``attention.varlen_ref``) lets no
+sequence see another's keys, so the gradients of one sequence's rows come
+from that sequence alone.
 """
 
 from __future__ import annotations
@@ -135,6 +139,41 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, *, window=(-1, -1
         if bounds:
             absd[1][b, :, c] = ak_acc
             absd[2][b, :, c] = av_acc
+    if bounds:
+        return tuple(out) + tuple(absd)
+    return tuple(out)
+
+
+def varlen_bwd_ref(q, k, v, do, cu_q, cu_k, scale: float, causal: bool, *, window=(-1, -1),
+                   kv_heads=None, bounds: bool = False):
+    """Gradients of ``varlen_ref``'s O: sequence b is rows cu_q[b] ..
+    cu_q[b+1]-1 of q, do [total_q, Hq, D] and rows cu_k[b] .. cu_k[b+1]-1 of
+    k, v [total_k, Hkv, D].  Returns (dq, dk, dv) in float64 with the shapes
+    of q, k, v (and, with ``bounds``, the |term| sums of attention_bwd_ref).
+    Keys of a sequence that no query row sees get dk = dv = 0.  ``kv_heads``
+    optionally restricts the work to (b, kv head) pairs; everything else is
+    NaN."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    cu_q = [int(x) for x in np.asarray(cu_q).reshape(-1)]
+    cu_k = [int(x) for x in np.asarray(cu_k).reshape(-1)]
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = Hq // Hkv
+    out = [np.full(q.shape, np.nan), np.full(k.shape, np.nan), np.full(v.shape, np.nan)]
+    absd = [np.full(x.shape, np.nan) for x in out] if bounds else None
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        sel = None if kv_heads is None else [(0, c) for (bb, c) in kv_heads if bb == b]
+        if sel is not None and not sel:
+            continue
+        res = attention_bwd_ref(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], do[None, q0:q1],
+                                scale, causal, window=window, kv_heads=sel, bounds=bounds)
+        cs = range(Hkv) if sel is None else [c for _, c in sel]
+        for c in cs:
+            hs = slice(c * g, (c + 1) * g)
+            for n, (lo, hi, hsl) in enumerate(((q0, q1, hs), (k0, k1, c), (k0, k1, c))):
+                out[n][lo:hi, hsl] = res[n][0, :, hsl]
+                if bounds:
+                    absd[n][lo:hi, hsl] = res[3 + n][0, :, hsl]
     if bounds:
         return tuple(out) + tuple(absd)
     return tuple(out)

@@ -36,7 +36,8 @@ def lib():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_decode",
+        ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size",
+         "fa_decode",
          "fa_decode_paged", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
 
 
@@ -209,6 +210,43 @@ def bwd(**kw):
 def test_bwd_rejects(lib, kw, status, text):
     assert bwd(**kw) == status
     assert text in _abi.fa_last_error()
+
+
+def bwd_ex(**kw):
+    a = dict(q=A16, k=A16, v=A16, o=A16, do=A16, lse=A16, dq=A16, dk=A16, dv=A16, cu_q=None,
+             cu_k=None, B=1, Hq=2, Hkv=1, Lq=8, Lk=8, total_q=0, total_k=0, D=64, scale=0.125,
+             causal=1, wl=-1, wr=-1, ws=A16, ws_bytes=1 << 30, dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_bwd_ex(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(cu_q=A16), _abi.FA_ERR_INVALID_ARGUMENT, "both be set"),
+    (dict(cu_k=A16), _abi.FA_ERR_INVALID_ARGUMENT, "both be set"),
+    (dict(cu_q=A16 + 2, cu_k=A16, total_q=8, total_k=8), _abi.FA_ERR_INVALID_ARGUMENT,
+     "4-byte aligned"),
+    (dict(cu_q=A16, cu_k=A16, total_q=0, total_k=8), _abi.FA_ERR_INVALID_ARGUMENT, "total_q=0"),
+    (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=0), _abi.FA_ERR_INVALID_ARGUMENT, "total_k=0"),
+    (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=8, D=256), _abi.FA_ERR_UNSUPPORTED,
+     "backward head_dim 256"),
+    (dict(cu_q=A16, cu_k=A16, total_q=1 << 30, total_k=8, Hq=4), _abi.FA_ERR_INVALID_ARGUMENT,
+     "exceeds 2^31-1"),
+    (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=8, ws_bytes=16), _abi.FA_ERR_INVALID_ARGUMENT,
+     "needs"),
+])
+def test_bwd_ex_rejects(lib, kw, status, text):
+    assert bwd_ex(**kw) == status
+    assert text in _abi.fa_last_error()
+
+
+def test_bwd_is_bwd_ex_without_offsets(lib):
+    """fa_bwd validates exactly as fa_bwd_ex with NULL offsets."""
+    for kw in (dict(B=0), dict(Hq=3, Hkv=2), dict(D=256), dict(scale=float("nan")),
+               dict(ws_bytes=16), dict(dk=A16 + 8)):
+        st1 = bwd(**kw)
+        e1 = _abi.fa_last_error()
+        st2 = bwd_ex(**kw)
+        assert (st1, e1) == (st2, _abi.fa_last_error())
 
 
 def test_bwd_workspace_size(lib):

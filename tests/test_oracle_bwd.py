@@ -185,3 +185,80 @@ def test_planted_mistake_in_group_sum_is_caught():
         except (AssertionError, ValueError, IndexError):
             failed.append(pin.__name__)
     assert failed
+
+
+# Packed sequences: (lengths q, lengths k) per case; causal / window inside each
+VARLEN_FD_CASES = [
+    (([2, 0, 3], [2, 2, 3]), 2, 1, 2, True, 0.8, (-1, -1)),    # an empty query sequence
+    (([3, 1, 2], [1, 3, 0]), 2, 2, 2, True, 0.6, (-1, -1)),    # Lk < Lq, Lk > Lq, no keys
+    (([4, 2], [4, 3]), 2, 1, 2, False, -0.7, (1, 0)),          # window, negative scale
+]
+
+
+def _packed(seed, lq, lk, Hq, Hkv, D):
+    rng = np.random.default_rng(seed)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    q = rng.standard_normal((cu_q[-1], Hq, D))
+    k = rng.standard_normal((cu_k[-1], Hkv, D))
+    v = rng.standard_normal((cu_k[-1], Hkv, D))
+    do = rng.standard_normal(q.shape)
+    return q, k, v, do, cu_q, cu_k
+
+
+def test_varlen_bwd_finite_differences():
+    pin_varlen_finite_differences(oracle.varlen_bwd_ref)
+
+
+def pin_varlen_finite_differences(fn):
+    """Central differences of the packed forward oracle (sum of O * dO)."""
+    h = 1e-6
+    for n, ((lq, lk), Hq, Hkv, D, causal, scale, win) in enumerate(VARLEN_FD_CASES):
+        q, k, v, do, cu_q, cu_k = _packed(1000 + n, lq, lk, Hq, Hkv, D)
+
+        def f(q_, k_, v_):
+            o, _ = oracle.varlen_ref(q_, k_, v_, cu_q, cu_k, scale, causal, window=win, workers=1)
+            return float(np.nansum(o * do))
+
+        dq, dk, dv = fn(q, k, v, do, cu_q, cu_k, scale, causal, window=win)
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                a = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                b = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (f(*a) - f(*b)) / (2 * h)
+            assert_close(grad, num, 2e-8, f"packed finite differences d{name} case {n}")
+
+
+def test_varlen_bwd_kv_head_selection_and_bounds():
+    q, k, v, do, cu_q, cu_k = _packed(1100, [5, 3], [4, 6], 4, 2, 3)
+    full = oracle.varlen_bwd_ref(q, k, v, do, cu_q, cu_k, 0.5, True, bounds=True)
+    part = oracle.varlen_bwd_ref(q, k, v, do, cu_q, cu_k, 0.5, True, kv_heads=[(1, 1)])
+    assert np.array_equal(part[0][5:, 2:4], full[0][5:, 2:4])
+    assert np.array_equal(part[1][4:, 1], full[1][4:, 1])
+    assert np.isnan(part[0][:5]).all() and np.isnan(part[2][:4]).all()
+    for x, a in zip(full[:3], full[3:]):
+        assert np.all(np.abs(x) <= a + 1e-15)
+
+
+VARLEN_MUTATIONS = {
+    "keys_at_query_rows": ("k[None, k0:k1], v[None, k0:k1], do[None, q0:q1]",
+                           "k[None, q0:q1], v[None, q0:q1], do[None, q0:q1]"),
+    "dk_written_to_query_rows": ("enumerate(((q0, q1, hs), (k0, k1, c), (k0, k1, c)))",
+                                 "enumerate(((q0, q1, hs), (q0, q1, c), (k0, k1, c)))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_MUTATIONS))
+def test_planted_mistake_in_varlen_backward_is_caught(name):
+    old, new = VARLEN_MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(obwd.varlen_bwd_ref))
+    assert old in src, f"mutation anchor not found: {old!r}"
+    ns = dict(vars(obwd))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        with np.errstate(all="ignore"):
+            pin_varlen_finite_differences(ns["varlen_bwd_ref"])
