@@ -130,7 +130,7 @@ def flash_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch
                    workspace=None):
     """Gradients of flash_attn_fwd: returns (dq [B,Lq,Hq,D], dk, dv [B,Lk,Hkv,D])
     in q's dtype from the forward's inputs, its output ``out`` and ``lse``,
-    and the output gradient ``dout``.  D in {64, 128}."""
+    and the output gradient ``dout``.  D in {64, 128, 256}."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse"), (dout, "dout")):
         _check_dev(t, n)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or out.shape != q.shape:
@@ -205,7 +205,7 @@ def flash_attn_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out
                           dk=None, dv=None, workspace=None):
     """Gradients of flash_attn_varlen for packed sequences: q, out, dout
     [total_q,Hq,D], k, v [total_k,Hkv,D], lse [Hq,total_q] float32 as the
-    forward wrote it.  Returns (dq, dk, dv) in q's dtype.  D in {64, 128}."""
+    forward wrote it.  Returns (dq, dk, dv) in q's dtype.  D in {64, 128, 256}."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (lse, "lse"), (dout, "dout"),
                  (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
         _check_dev(t, n)

@@ -317,8 +317,8 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)dtype);
-  if (D != 64 && D != 128)
-    return fail(FA_ERR_UNSUPPORTED, "backward head_dim %d not in {64, 128}", D);
+  if (!head_dim_supported(D))
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", D);
   if ((long long)Hq * D >= (1LL << 25) || (long long)Hkv * D >= (1LL << 25))
     return fail(FA_ERR_INVALID_ARGUMENT, "Hq * D and Hkv * D must be < 2^25");
   const long long rows_q = packed ? (long long)total_q : (long long)B * Lq;
@@ -327,8 +327,8 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
       (long long)B * Lq * Hq > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H (rows * heads) exceeds 2^31-1");
   if (((long long)Lq + 127) / 128 * B * Hq > 0x7fffffffLL ||
-      ((long long)Lk + 127) / 128 * B * Hkv > 0x7fffffffLL)
-    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (L/128 * B * H > 2^31-1)");
+      ((long long)Lk + 63) / 64 * B * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (Lq/128 * B * Hq or Lk/64 * B * Hkv > 2^31-1)");
   const long long span = rows_q + rows_k;
   const bool windowed = window_left >= 0 || window_right >= 0;
   if (windowed && span > (1LL << 30))
@@ -367,7 +367,7 @@ const char* fa_info(void) {
          "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), 32-key tiles, "
          "mfma_f32_32x32x16, LDS-direct K/V with transpose reads, causal/window tile "
          "skip, block-diagonal packing, GQA; "
-         "bwd: dQ query-major, dK/dV key-major in pairs of waves, dense and packed; "
+         "bwd: dQ query-major, dK/dV key-major in pairs of waves, dense and packed, D={64,128,256}; "
          "decode: split-KV, 4 wave64 per (chunk, kv head, 16 heads, sequence), 16-key steps, "
          "mfma_f32_16x16x32 + 16x16x16, logsumexp combine, paged and int8 KV caches; "
          "version=0.4.0";

@@ -240,7 +240,7 @@ __device__ __forceinline__ f32x16 mfma_tr(const uint16_t* tile, const int (&toff
 // dQ: query-major.
 // -------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBT, 2)
+__global__ __launch_bounds__(kBT, (D <= 128 ? 2 : 1))
 void bwd_dq_kernel(const BwdParams p) {
   constexpr int BN = kTile;
   constexpr int TILE = BN * D;
@@ -380,25 +380,28 @@ void bwd_dq_kernel(const BwdParams p) {
 // -------------------------------------------------------------------------
 // dK, dV: key-major, waves in pairs.
 // -------------------------------------------------------------------------
-constexpr int kKW = 8;         // waves per dK/dV workgroup: 4 pairs x 32 keys
-constexpr int kKT = kKW * 64;  // threads per dK/dV workgroup
+// Waves per dK/dV workgroup (pairs x 32 keys): 8, two per SIMD, where a
+// wave's accumulator and operand fit 256 registers (D <= 128); 4, one per SIMD
+// with 512 registers, at D = 256.
+template <int D> struct KvWaves { static constexpr int value = D <= 128 ? 8 : 4; };
 
 // LDS-direct copy of one query tile of Q and of dO (ROWS x D each; rows past
-// `last` re-read `last`) by all the waves of a dK/dV workgroup: load i of
-// thread t moves chunk (i * 8 + wave) * 64 + lane of the list [Q chunks, dO
+// `last` re-read `last`) by all the NW waves of a dK/dV workgroup: load i of
+// thread t moves chunk (i * NW + wave) * 64 + lane of the list [Q chunks, dO
 // chunks], 16-byte chunks XOR-swizzled by row as in TileLoader.
 template <int D, int ROWS>
 struct PairTileLoader {
+  static constexpr int NW = KvWaves<D>::value;
   static constexpr int CPR = D / 8;
   static constexpr int QCH = ROWS * CPR;  // chunks per tile
-  static constexpr int NLOAD = 2 * QCH / kKT;
-  static_assert((2 * QCH) % kKT == 0 && QCH % 64 == 0, "tile shape");
+  static constexpr int NLOAD = 2 * QCH / (NW * 64);
+  static_assert((2 * QCH) % (NW * 64) == 0 && QCH % 64 == 0, "tile shape");
   uint32_t off[NLOAD];
   int rr[NLOAD];
   __device__ __forceinline__ void init(int wu, int lane, int stride) {
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
-      const int P = (i * kKW + wu) * 64 + lane;
+      const int P = (i * NW + wu) * 64 + lane;
       const int c = P < QCH ? P : P - QCH;
       const int r = c / CPR, pc = c % CPR;
       rr[i] = r;
@@ -411,7 +414,7 @@ struct PairTileLoader {
     const bool whole = r0 + ROWS - 1 <= last;
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
-      const int c0 = (i * kKW + wu) * 64;  // wave-uniform first chunk
+      const int c0 = (i * NW + wu) * 64;  // wave-uniform first chunk
       const bool isg = c0 >= QCH;
       uint32_t o = off[i];
       if (!whole) o -= 2u * (uint32_t)(((r0 + rr[i]) - min(r0 + rr[i], last)) * stride);
@@ -420,8 +423,8 @@ struct PairTileLoader {
   }
 };
 
-// A workgroup owns 128 keys of one K/V head: 4 pairs of waves, 32 keys per
-// pair (one per lane column).  It streams tiles of 32 query rows of every
+// A workgroup owns 16 * NW keys of one K/V head: NW / 2 pairs of waves, 32
+// keys per pair (one per lane column).  It streams tiles of 32 query rows of every
 // query head of the group (Q, dO, lse, D) through LDS.  Within a pair the
 // work of a tile is split so that each wave holds one 32 x D accumulator and
 // one operand, which keeps two waves per SIMD resident:
@@ -434,8 +437,10 @@ struct PairTileLoader {
 // The partner's lag keeps the previous tile's Q in LDS: three stages of Q /
 // dO tiles (current, previous, next) and two of the P exchange.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kKT, 1)
+__global__ __launch_bounds__(KvWaves<D>::value * 64, 1)
 void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int NW = KvWaves<D>::value;
+  constexpr int KBM = NW / 2 * kBR;  // keys per workgroup
   constexpr int BQ = kTile;
   constexpr int TILE = BQ * D;
   // Distinct arrays per stage: the compiler then sees that reading one stage
@@ -450,7 +455,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sL1[2 * BQ];
   __shared__ __attribute__((aligned(16))) float sL2[2 * BQ];
   // P exchange: [step parity][pair][4 x 64 lanes x 4 floats]
-  __shared__ __attribute__((aligned(16))) float sX[2][kKW / 2][16 * 64];
+  __shared__ __attribute__((aligned(16))) float sX[2][NW / 2][16 * 64];
   auto qst = [&](auto I) -> uint16_t* {
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return sQ0; else if constexpr (i == 1) return sQ1; else return sQ2;
@@ -470,19 +475,19 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int pair = wu >> 1;
-  // Role per wave, alternated so that each SIMD (wave w runs on SIMD w % 4)
-  // gets one wave of each kind: 1 = the dS / dK wave.
+  // Role per wave, alternated so that with 8 waves each SIMD (wave w runs on
+  // SIMD w % 4) gets one wave of each kind: 1 = the dS / dK wave.
   const bool sw = ((wu & 1) ^ ((wu >> 2) & 1)) != 0;
   // Key tiles ascending: under a causal mask the first see the most queries.
   int b, kvh, kt;
   bwd_item(p.B, Hkv, b, kvh, kt);
   const SeqRows sr = seq_rows(p, b);
   const int Lq = sr.Lq, Lk = sr.Lk;
-  const int k0 = kt * kBM;
+  const int k0 = kt * KBM;
   if (k0 >= Lk) return;  // past this sequence's keys (whole workgroup)
   const int shift = Lk - Lq;
   const int kw0 = k0 + kBR * pair, key = kw0 + l32;
-  const int k_last = min(k0 + kBM, Lk) - 1;
+  const int k_last = min(k0 + KBM, Lk) - 1;
   const int kw_last = min(kw0 + kBR - 1, Lk - 1);
   const int wl = p.win_left, wr = p.win_right;
   auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
@@ -712,15 +717,16 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gq((unsigned)((long)((a.Lq + kBM - 1) / kBM) * a.Hq * a.B));
-  const dim3 gk((unsigned)((long)((a.Lk + kBM - 1) / kBM) * a.Hkv * a.B));
+  constexpr int NW = KvWaves<D>::value, KBM = NW / 2 * kBR;
+  const dim3 gk((unsigned)((long)((a.Lk + KBM - 1) / KBM) * a.Hkv * a.B));
   if (a.causal) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), gq, dim3(kBT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), gk, dim3(kKT), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), gk, dim3(NW * 64), 0, stream, p);
   } else {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), gq, dim3(kBT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), gk, dim3(kKT), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), gk, dim3(NW * 64), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -730,6 +736,7 @@ hipError_t launch_bwd_dtype(const BwdArgs& a, hipStream_t stream) {
   switch (a.D) {
     case 64: return launch_bwd_t<T, 64>(a, stream);
     case 128: return launch_bwd_t<T, 128>(a, stream);
+    case 256: return launch_bwd_t<T, 256>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

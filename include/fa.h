@@ -247,8 +247,7 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Lq);
  *   dq          device [B, Lq, Hq, D] (dtype), written.
  *   dk, dv      device [B, Lk, Hkv, D] (dtype), written (summed over each
  *               K/V head's query heads).
- *   D           64 or 128 (256: FA_ERR_UNSUPPORTED -- the two D x 32 fp32
- *               accumulators per wave do not fit the register file).
+ *   D           64, 128 or 256 (others: FA_ERR_UNSUPPORTED).
  *   causal, window_left, window_right, scale: as in fa_fwd_ex; must be the
  *               forward's.
  *   workspace   fa_bwd_workspace_size(B, Hq, Lq) bytes, 16-byte aligned,

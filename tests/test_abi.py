@@ -201,7 +201,7 @@ def bwd(**kw):
     (dict(dk=A16 + 8), _abi.FA_ERR_INVALID_ARGUMENT, "dk is not 16-byte aligned"),
     (dict(ws=None), _abi.FA_ERR_INVALID_ARGUMENT, "workspace is NULL"),
     (dict(ws_bytes=16), _abi.FA_ERR_INVALID_ARGUMENT, "needs"),
-    (dict(D=256), _abi.FA_ERR_UNSUPPORTED, "backward head_dim 256"),
+    (dict(D=96), _abi.FA_ERR_UNSUPPORTED, "head_dim 96"),
     (dict(Hq=3, Hkv=2), _abi.FA_ERR_INVALID_ARGUMENT, "not a multiple"),
     (dict(Lk=0), _abi.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1"),
     (dict(scale=float("inf")), _abi.FA_ERR_INVALID_ARGUMENT, "not finite"),
@@ -227,8 +227,8 @@ def bwd_ex(**kw):
      "4-byte aligned"),
     (dict(cu_q=A16, cu_k=A16, total_q=0, total_k=8), _abi.FA_ERR_INVALID_ARGUMENT, "total_q=0"),
     (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=0), _abi.FA_ERR_INVALID_ARGUMENT, "total_k=0"),
-    (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=8, D=256), _abi.FA_ERR_UNSUPPORTED,
-     "backward head_dim 256"),
+    (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=8, D=32), _abi.FA_ERR_UNSUPPORTED,
+     "head_dim 32"),
     (dict(cu_q=A16, cu_k=A16, total_q=1 << 30, total_k=8, Hq=4), _abi.FA_ERR_INVALID_ARGUMENT,
      "exceeds 2^31-1"),
     (dict(cu_q=A16, cu_k=A16, total_q=8, total_k=8, ws_bytes=16), _abi.FA_ERR_INVALID_ARGUMENT,
@@ -241,7 +241,7 @@ def test_bwd_ex_rejects(lib, kw, status, text):
 
 def test_bwd_is_bwd_ex_without_offsets(lib):
     """fa_bwd validates exactly as fa_bwd_ex with NULL offsets."""
-    for kw in (dict(B=0), dict(Hq=3, Hkv=2), dict(D=256), dict(scale=float("nan")),
+    for kw in (dict(B=0), dict(Hq=3, Hkv=2), dict(D=96), dict(scale=float("nan")),
                dict(ws_bytes=16), dict(dk=A16 + 8)):
         st1 = bwd(**kw)
         e1 = _abi.fa_last_error()

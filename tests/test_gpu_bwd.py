@@ -74,7 +74,7 @@ RAGGED = [(1, 1), (17, 17), (64, 64), (65, 65), (129, 129), (300, 300), (65, 200
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("Lq,Lk", RAGGED, ids=[f"{a}x{b}" for a, b in RAGGED])
 def test_bwd_ragged(Lq, Lk, D, dtype, causal, gpu):
     check(1, Lq, Lk, 4, 2, D, dtype, causal, seed=Lq * 31 + Lk + D, gpu=gpu)
@@ -93,6 +93,27 @@ WINDOWS = [(0, 0), (5, 3), (64, -1), (-1, 40)]
 def test_bwd_windows(window, causal, gpu):
     check(1, 300, 300, 4, 2, 64, torch.bfloat16, causal, seed=7 + window[0], gpu=gpu,
           window=window)
+
+
+def test_bwd_d256_gqa_window(gpu):
+    check(2, 200, 333, 8, 2, 256, torch.float16, True, seed=81, gpu=gpu)
+    check(1, 300, 300, 4, 1, 256, torch.bfloat16, False, seed=82, gpu=gpu, window=(40, 9))
+
+
+def test_bwd_d256_full_size_sampled(gpu):
+    """The d256 workload (B=2, H=16, L=4096, D=256, fp16, causal); the oracle
+    computes two whole heads' gradients."""
+    cfg = W.PREFILL["d256"]
+    q, k, v = W.prefill_inputs(cfg)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(cfg.seed + 100)).to(cfg.dtype)
+    scale = f32(cfg.scale)
+    say("bwd full-size d256")
+    dq, dk, dv = run_bwd(q, k, v, do, scale, True, (-1, -1), gpu)
+    heads = [(0, 0), (cfg.B - 1, cfg.Hkv - 1)]
+    r = oracle.attention_bwd_ref(q, k, v, do, scale, True, bounds=True, kv_heads=heads)
+    compare_grad(dq, r[0], r[3], cfg.dtype, f"dq {heads}")
+    compare_grad(dk, r[1], r[4], cfg.dtype, f"dk {heads}")
+    compare_grad(dv, r[2], r[5], cfg.dtype, f"dv {heads}")
 
 
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
@@ -134,7 +155,7 @@ def test_bwd_full_size_sampled(gpu):
 def test_bwd_errors(gpu):
     from exact_tiled_attention_fa_amd.attention import FAError, flash_attn_bwd
 
-    q = torch.zeros((1, 8, 2, 256), dtype=torch.bfloat16, device=gpu)
+    q = torch.zeros((1, 8, 2, 96), dtype=torch.bfloat16, device=gpu)
     lse = torch.zeros((1, 2, 8), dtype=torch.float32, device=gpu)
     with pytest.raises(FAError, match="FA_ERR_UNSUPPORTED"):
         flash_attn_bwd(q, q, q, q, lse, q)

@@ -73,6 +73,12 @@ def test_varlen_bwd(case, D, causal, window, gpu):
     check(lens_q, lens_k, 8, 2, D, dtype, causal, window, 11 * case + D, gpu)
 
 
+def test_varlen_bwd_d256(gpu):
+    check([1, 130, 0, 257, 64], [5, 130, 3, 300, 64], 4, 2, 256, torch.float16, True, (-1, -1),
+          90, gpu)
+    check([300, 17], [129, 500], 4, 4, 256, torch.bfloat16, False, (32, 8), 91, gpu)
+
+
 @pytest.mark.parametrize("g", [1, 4])
 def test_varlen_bwd_gqa(g, gpu):
     check([200, 65, 129], [200, 65, 129], 8, 8 // g, 128, torch.bfloat16, True, (-1, -1), 60 + g,
