@@ -491,8 +491,11 @@ void fwd_kernel(const FwdParams prm) {
       const int row = p / CPR, c = p % CPR;
       const int q = qw0 + row;
       if (q < Lq)
-        store16(prm.O + ((long)qs + q) * qstride + (long)h * D + 8 * c,
-                *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))));
+        // non-temporal: O is written once and not read back here (whole
+        // rows per instruction, so no line is written in pieces)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))),
+            reinterpret_cast<u32x4*>(prm.O + ((long)qs + q) * qstride + (long)h * D + 8 * c));
     }
   } else if (qrow < Lq) {
     uint16_t* Orow = prm.O + ((long)qs + qrow) * qstride + (long)h * D;
@@ -509,7 +512,8 @@ void fwd_kernel(const FwdParams prm) {
   if (hf == 0 && qrow < Lq) {
     // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
     const long li = prm.cu_q ? (long)h * prm.total_q + qs + qrow : ((long)bh * Lq + qrow);
-    prm.LSE[li] = l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
+    __builtin_nontemporal_store(
+        l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY, prm.LSE + li);
   }
 }
 
