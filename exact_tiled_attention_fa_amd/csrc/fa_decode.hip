@@ -15,16 +15,18 @@
 // kv head, group of <= 16 query heads, sequence).  The chunk is walked in
 // 16-key steps; wave w takes steps w, w+4, ..., so a long chunk is four short
 // serial chains.  Per step:
-//   * S^T = K q^T with v_mfma_f32_16x16x32: A = the 16 key rows straight from
-//     registers, B = q^T (the group's heads as 16 columns, zero-padded).  The
-//     accumulator gives each lane one head and four consecutive keys.
+//   * S^T = K q^T with v_mfma_f32_16x16x32: A = the 16 key rows read from the
+//     wave's LDS K tile, B = q^T (the group's heads as 16 columns,
+//     zero-padded).  The accumulator gives each lane one head and four
+//     consecutive keys.
 //   * O^T += V^T P^T with v_mfma_f32_16x16x16: its B operand is exactly that
 //     accumulator layout (rounded to 16 bits), and its A operand, four keys of
 //     one head-dim column per lane, is one ds_read_b64_tr_b16 of the V tile.
 //   * K and V rows of step i+1 are loaded into registers while step i
-//     computes; V is written row-major into the wave's own small LDS tile (no
-//     barrier: only that wave reads it).  All loads go through VGPRs, so the
-//     compiler's wait counts stay exact and the prefetch is never drained.
+//     computes, whole rows per load instruction, non-temporal; both are
+//     written row-major into the wave's own small LDS tiles (no barrier: only
+//     that wave reads them).  All loads go through VGPRs, so the compiler's
+//     wait counts stay exact and the prefetch is never drained.
 // At the end the four waves' (O, lse) are merged through LDS.  Workspace:
 // float32 partial outputs [B, Hq, S, D], then float32 partial logsumexps in
 // base 2 [B, Hq, S].
@@ -78,11 +80,11 @@ struct SplitParams {
 };
 
 // Eight int8 codes (two dwords) widened exactly to eight 16-bit values.
-// V rows are read exactly once per call, each load instruction covering
+// K and V rows are read exactly once per call, each load instruction covering
 // whole rows: non-temporal loads stream them past the caches (on the MI355X a
 // plain 16-byte streaming read reaches about 6.3 TB/s, a non-temporal one
-// about 7.1 TB/s).  K loads cover half a cache line each (the other half comes
-// with the next instruction) and stay cached.
+// about 7.1 TB/s).  A non-temporal load that fetches a line in pieces is
+// slower instead, which is why K is not loaded in the MFMA operand layout.
 template <typename V> __device__ __forceinline__ V stream_load(const V* p) {
   return __builtin_nontemporal_load(p);
 }
@@ -114,6 +116,13 @@ void decode_split_kernel(const SplitParams prm) {
   constexpr int WS = VT > MERGE ? VT : MERGE;
   __shared__ __attribute__((aligned(16))) uint16_t sV[kDW][WS];
   __shared__ float sL[kDW][16];
+  // Per-wave K tile [16][D] (16-bit or int8 codes), 16-byte chunks XOR-swizzled by row.
+  constexpr int KEB = KI8 ? 1 : 2;         // bytes per cached K element
+  constexpr int KLPR = D * KEB / 16;       // 16-byte K loads per row
+  constexpr int NKL = kKS * KLPR / 64;     // 16-byte K loads per lane per step
+  constexpr int KSW = (KLPR < 16 ? KLPR : 16) - 1;
+  static_assert(NKL >= 1, "K tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t sKt[kDW][kKS * D * KEB];
 
   const int split = blockIdx.x;
   const int b = blockIdx.z;
@@ -200,13 +209,17 @@ void decode_split_kernel(const SplitParams prm) {
   auto row_off = [&](const StepRows& st, int i) {
     return (uint32_t)(min(i, k1 - 1 - st.first) * (int)kstride);
   };
-  using KX = std::conditional_t<KI8, u32x2, u32x4>;
-  auto kload = [&](const StepRows& st, KX (&kx)[D / 32], f32x4& ksc) {
-    const KE* kr = Kb + st.row0 * kstride + row_off(st, l16);
+  // K rows are read like V rows, whole rows per instruction (16 lanes per row
+  // of 16-bit elements), with non-temporal loads, and staged through the
+  // wave's LDS tile: the MFMA operand layout would fetch half a cache line
+  // per instruction.
+  auto kload = [&](const StepRows& st, u32x4 (&kx)[NKL], f32x4& ksc) {
+    const KE* kr = Kb + st.row0 * kstride;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      if constexpr (KI8) kx[ks] = *reinterpret_cast<const u32x2*>(kr + 32 * ks + 8 * q4);
-      else kx[ks] = load16(kr + 32 * ks + 8 * q4);
+    for (int i = 0; i < NKL; ++i) {
+      const int P = 64 * i + lane;
+      kx[i] = stream_load(
+          reinterpret_cast<const u32x4*>(kr + row_off(st, P / KLPR) + (16 / KEB) * (P % KLPR)));
     }
     // scales of keys first + 4*q4 .. +3 (the score layout below); slots past
     // the chunk end hold anything and are masked
@@ -224,12 +237,21 @@ void decode_split_kernel(const SplitParams prm) {
     }
     if constexpr (VI8) vsc = *reinterpret_cast<const f32x4*>(prm.vsc + st.srow + 4 * q4);
   };
-  auto load_step = [&](int j, KX (&kx)[D / 32], f32x4& ksc, u32x4 (&vx)[NVL], f32x4& vsc) {
+  auto load_step = [&](int j, u32x4 (&kx)[NKL], f32x4& ksc, u32x4 (&vx)[NVL], f32x4& vsc) {
     const StepRows st = step_rows(j);
     kload(st, kx, ksc);
     vload(st, vx, vsc);
   };
   uint16_t* const sv = sV[w];
+  uint8_t* const sk = sKt[w];
+  auto kstore = [&](const u32x4 (&kx)[NKL]) {
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) {
+      const int P = 64 * i + lane;
+      const int r = P / KLPR, c = P % KLPR;
+      *reinterpret_cast<u32x4*>(sk + 16 * (r * KLPR + (c ^ (r & KSW)))) = kx[i];
+    }
+  };
   // Row-major V tile [16][D] of 16-bit values with 16-byte chunks
   // XOR-swizzled by row (int8 codes are widened on the way in).
   auto vstore = [&](const u32x4 (&vx)[NVL]) {
@@ -262,15 +284,25 @@ void decode_split_kernel(const SplitParams prm) {
   float m_ref = -INFINITY;
   float l_part = 0.f;
 
-  auto compute = [&](int j, const KX (&kx)[D / 32], const f32x4& ksc, const u32x4 (&vx)[NVL],
+  auto compute = [&](int j, const u32x4 (&kx)[NKL], const f32x4& ksc, const u32x4 (&vx)[NVL],
                      const f32x4& vsc) {
-    vstore(vx);  // the previous step's transpose reads of the tile are done (in-order LDS)
-    // S^T: keys 4*q4 + r (rows) x heads (columns l16).
+    // the previous step's reads of both tiles are done (in-order LDS)
+    kstore(kx);
+    vstore(vx);
+    // S^T: keys 4*q4 + r (rows) x heads (columns l16); lane (l16, q4) takes
+    // dims 32*ks + 8*q4 .. +7 of key row l16.
     f32x4 s = (f32x4){};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      if constexpr (KI8) s = Ops<T>::mfma16(widen8<T>(kx[ks]), qf[ks], s);
-      else s = Ops<T>::mfma16(kx[ks], qf[ks], s);
+      if constexpr (KI8) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(
+            sk + 16 * (l16 * KLPR + ((2 * ks + (q4 >> 1)) ^ (l16 & KSW))) + 8 * (q4 & 1));
+        s = Ops<T>::mfma16(widen8<T>(a), qf[ks], s);
+      } else {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(
+            sk + 16 * (l16 * KLPR + ((4 * ks + q4) ^ (l16 & KSW))));
+        s = Ops<T>::mfma16(a, qf[ks], s);
+      }
     }
     if constexpr (KI8) s *= ksc;  // each key row's scale
     const int lim = k1 - 1 - (k0 + kKS * j) - 4 * q4;  // key offset r visible iff <= lim
@@ -316,7 +348,7 @@ void decode_split_kernel(const SplitParams prm) {
   // step computes.  The request is unconditional (past the last step it
   // re-reads the chunk's final row, a cache hit) so that the number of loads
   // in flight, and thus each wait, is the same on every path.
-  KX kA[D / 32], kB[D / 32];
+  u32x4 kA[NKL], kB[NKL];
   u32x4 vA[NVL], vB[NVL];
   f32x4 kscA = {}, kscB = {}, vscA = {}, vscB = {};
   load_step(w, kA, kscA, vA, vscA);  // (a wave with no step reads the chunk's last step, unused)
