@@ -397,7 +397,7 @@ void decode_split_kernel(const SplitParams prm) {
       o /= tot;
     }
     const long pi = pbase + (long)hs * S;
-    Opart[pi * D + d] = o;
+    __builtin_nontemporal_store(o, Opart + pi * D + d);  // read once, by the merge
     if (d == 0) Lpart[pi] = M != -INFINITY ? M + __builtin_log2f(tot) : -INFINITY;
   }
 }
@@ -419,7 +419,7 @@ void decode_combine_kernel(const float* __restrict__ Opart, const float* __restr
       if (ls == -INFINITY) continue;
       const float wgt = exp2_fast(ls - M);
       tot += wgt;
-      out += wgt * Opart[(bh * S + s) * D + d];
+      out += wgt * __builtin_nontemporal_load(Opart + (bh * S + s) * D + d);
     }
     out /= tot;
   }
