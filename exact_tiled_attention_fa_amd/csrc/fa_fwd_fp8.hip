@@ -26,6 +26,8 @@
 //     to a factor of 2^0.5 so that 256 * P stays below e4m3's 448.  The row sum
 //     adds the unrounded fp32 probabilities.
 //   * K and V^T tiles stream HBM -> LDS with LDS-direct copies, two stages.
+//   * O is staged through the tile arrays and written as whole rows with
+//     non-temporal stores.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -260,20 +262,39 @@ void fwd_fp8_kernel(const Fp8Params prm) {
 
   const float l = sum_halves(l_part);
   const float inv = l > 0.f ? prm.oscale / l : 0.f;
-  if (qrow < Lq) {
-    uint16_t* out = prm.O + ((long)b * Lq + qrow) * qstride + (long)h * D;
+  // O = acc / l staged through LDS (wave w takes one of the four tile arrays,
+  // rows [32][D] of 16-bit values with 16-byte chunks XOR-swizzled by row) and
+  // written as whole rows with non-temporal stores; lse = ln2 * (m*scale2 +
+  // log2 l).
+  constexpr int CPR = D / 8;
+  constexpr int OSW = CPR < 16 ? CPR - 1 : 15;
+  static_assert(32 * D * 2 <= KT, "O stage");
+  __syncthreads();  // every copy has landed and all waves are done with the tiles
+  uint16_t* so = reinterpret_cast<uint16_t*>((w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 val = {Ops<OT>::pack2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
-                           Ops<OT>::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(out + 32 * db + 8 * g + 4 * hf) = val;
-      }
-    if (hf == 0)
-      prm.LSE[((long)b * Hq + h) * Lq + qrow] =
-          l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * hf;
+      const u32x2 val = {Ops<OT>::pack2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
+                         Ops<OT>::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+      *reinterpret_cast<u32x2*>(so + l32 * D + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int p = lane + 64 * i;
+    const int row = p / CPR, c = p % CPR;
+    const int q = qw0 + row;
+    if (q < Lq)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))),
+          reinterpret_cast<u32x4*>(prm.O + ((long)b * Lq + q) * qstride + (long)h * D + 8 * c));
   }
+  if (hf == 0 && qrow < Lq)
+    __builtin_nontemporal_store(
+        l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY,
+        prm.LSE + ((long)b * Hq + h) * Lq + qrow);
 }
 
 template <int D, typename OT>
