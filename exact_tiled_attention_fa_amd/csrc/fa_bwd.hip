@@ -115,8 +115,9 @@ void bwd_prep_kernel(const BwdParams p) {
   const long mrow = (long)(sr.qs + i) * p.Hq + h;  // row of O / dO in memory
   float acc = 0.f;
   if (valid) {
-    const u32x4 o = load16(p.O + mrow * D + 8 * c);
-    const u32x4 g = load16(p.dO + mrow * D + 8 * c);
+    // read once here: non-temporal (whole rows per group of CPR lanes)
+    const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.O + mrow * D + 8 * c));
+    const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.dO + mrow * D + 8 * c));
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       acc += Ops<T>::lo(o[e]) * Ops<T>::lo(g[e]) + Ops<T>::hi(o[e]) * Ops<T>::hi(g[e]);
@@ -234,6 +235,41 @@ __device__ __forceinline__ f32x16 mfma_tr(const uint16_t* tile, const int (&toff
   const u32x2 lo = lds_read_tr16(tile + 16 * ts * D + toff[db][0]);
   const u32x2 hi = lds_read_tr16(tile + 16 * ts * D + toff[db][1]);
   return Ops<T>::mfma32((u32x4){lo[0], lo[1], hi[0], hi[1]}, bop, acc);
+}
+
+// Writes a wave's 32 x D accumulator (lane column l32 = row r0 + l32, element
+// 4g + i of block db = column 32db + 8g + 4(lane/32) + i) times `sc` as 16-bit
+// rows r0 .. r0+31 (those below `rows`) of a matrix with row stride `stride`:
+// staged in the wave's LDS area `so` (32 x D, 16-byte chunks XOR-swizzled by
+// row) and stored as whole rows with non-temporal stores.  The workgroup
+// barriers keep the areas clear of the tiles' last reads.
+template <typename T, int D>
+__device__ __forceinline__ void stage_rows(const f32x16 (&acc)[D / 32], float sc, uint16_t* so,
+                                           int lane, uint16_t* base, long stride, int r0,
+                                           int rows) {
+  constexpr int CPR = D / 8;
+  constexpr int OSW = CPR < 16 ? CPR - 1 : 15;
+  const int l32 = lane & 31, hf = lane >> 5;
+  __syncthreads();  // every copy has landed and all waves are done with the tiles
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * hf;
+      const u32x2 val = {Ops<T>::pack2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
+                         Ops<T>::pack2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
+      *reinterpret_cast<u32x2*>(so + l32 * D + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int pp = lane + 64 * i;
+    const int row = pp / CPR, c = pp % CPR;
+    if (r0 + row < rows)
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))),
+          reinterpret_cast<u32x4*>(base + (long)(r0 + row) * stride + 8 * c));
+  }
 }
 
 // -------------------------------------------------------------------------
@@ -363,18 +399,11 @@ void bwd_dq_kernel(const BwdParams p) {
     }
   }
 
-  if (qrow < Lq) {
-    uint16_t* out = p.dQ + ((long)sr.qs + qrow) * qstride + (long)h * D;
-    const float sc = p.scale;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 val = {Ops<T>::pack2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
-                           Ops<T>::pack2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
-        *reinterpret_cast<u32x2*>(out + 32 * db + 8 * g + 4 * hf) = val;
-      }
-  }
+  // dQ staged through LDS (wave w takes one of the four tile arrays, rows
+  // [32][D] with 16-byte chunks XOR-swizzled by row) and written as whole
+  // rows with non-temporal stores.
+  stage_rows<T, D>(acc, p.scale, (w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1, lane,
+                   p.dQ + (long)sr.qs * qstride + (long)h * D, qstride, qw0, Lq);
 }
 
 // -------------------------------------------------------------------------
@@ -664,20 +693,14 @@ void bwd_dkdv_kernel(const BwdParams p) {
       run(std::false_type{});
   }
 
-  if (key < Lk) {
-    const long orow = ((long)sr.ks + key) * kstride + (long)kvh * D;
-    uint16_t* out = (sw ? p.dK : p.dV) + orow;
-    const float sc = sw ? p.scale : 1.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int d = 32 * db + 8 * gg + 4 * hf;
-        *reinterpret_cast<u32x2*>(out + d) =
-            (u32x2){Ops<T>::pack2(acc[db][4 * gg] * sc, acc[db][4 * gg + 1] * sc),
-                    Ops<T>::pack2(acc[db][4 * gg + 2] * sc, acc[db][4 * gg + 3] * sc)};
-      }
-  }
+  // dK (dS waves) or dV (P waves) staged through LDS, one tile-sized area
+  // per wave, and written as whole rows with non-temporal stores.
+  static_assert(NW <= 6 || sizeof(sX) >= 2 * TILE * sizeof(uint16_t), "dK/dV stage");
+  uint16_t* const sxo = reinterpret_cast<uint16_t*>(&sX[0][0][0]);
+  uint16_t* const so = wu == 0 ? sQ0 : wu == 1 ? sG0 : wu == 2 ? sQ1 : wu == 3 ? sG1
+                     : wu == 4 ? sQ2 : wu == 5 ? sG2 : wu == 6 ? sxo : sxo + TILE;
+  stage_rows<T, D>(acc, sw ? p.scale : 1.f, so, lane,
+                   (sw ? p.dK : p.dV) + (long)sr.ks * kstride + (long)kvh * D, kstride, kw0, Lk);
 }
 
 template <typename T, int D>
