@@ -114,9 +114,8 @@ void fwd_kernel(const FwdParams prm) {
   constexpr int TILE = BN * D;               // elements per K or V tile
   constexpr int NLOAD = BN * CPR / kNT;      // LDS-direct loads per thread per tile (each of K, V)
   static_assert(BN % 32 == 0 && D % 32 == 0 && (BN * CPR) % kNT == 0, "tile shape");
-  // The output is staged through LDS (one tile array per wave) when four
-  // waves' 32 x D tiles fit; otherwise it is stored straight from registers.
-  constexpr bool kStageO = kFwdWaves == 4 && 32 * D <= TILE;
+  // The output is staged through LDS, one K/V tile array per wave.
+  static_assert(kFwdWaves == 4 && 32 * D <= TILE, "O stage");
   // kStages stages of K and V tiles.  Distinct arrays (not slices of one)
   // let the compiler see that reading one stage does not alias the
   // LDS-direct copy into another, so it inserts no wait between them.
@@ -472,7 +471,7 @@ void fwd_kernel(const FwdParams prm) {
   const float l = sum_halves(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   constexpr int OSW = CPR < 16 ? CPR - 1 : 15;
-  if constexpr (kStageO) {
+  {
     __syncthreads();  // all waves are done with the K/V tiles
     uint16_t* so = (w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1;
 #pragma unroll
@@ -497,17 +496,6 @@ void fwd_kernel(const FwdParams prm) {
             *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))),
             reinterpret_cast<u32x4*>(prm.O + ((long)qs + q) * qstride + (long)h * D + 8 * c));
     }
-  } else if (qrow < Lq) {
-    uint16_t* Orow = prm.O + ((long)qs + qrow) * qstride + (long)h * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d = 32 * db + 8 * a4 + 4 * hf;
-        u32x2 val = {Ops<T>::pack2(acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv),
-                     Ops<T>::pack2(acc[db][4 * a4 + 2] * inv, acc[db][4 * a4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(Orow + d) = val;
-      }
   }
   if (hf == 0 && qrow < Lq) {
     // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
