@@ -193,10 +193,13 @@ def cpu_baseline_decode(cfg, q, kc, vc, lens, scale, nseq=16):
     import oracle
     from exact_tiled_attention_fa_amd import workloads as W
 
+    from threadpoolctl import threadpool_limits
+
     heads = [(b, h) for b in range(nseq) for h in range(cfg.Hq)]
-    t0 = time.perf_counter()
-    oracle.decode_ref(q, kc, vc, lens, scale, heads=heads)
-    dt = time.perf_counter() - t0
+    with threadpool_limits(limits=1):  # the oracle's decode is one thread; so is its BLAS
+        t0 = time.perf_counter()
+        oracle.decode_ref(q, kc, vc, lens, scale, heads=heads)
+        dt = time.perf_counter() - t0
     sub = lens[:nseq]
     byts = int(sum(int(x) for x in sub)) * cfg.Hkv * cfg.D * 2 * 2 + nseq * cfg.Hq * (2 * cfg.D * 2 + 4)
     return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
