@@ -276,3 +276,26 @@ def fp8(**kw):
 def test_fp8_rejects(lib, kw, status, text):
     assert fp8(**kw) == status
     assert text in _abi.fa_last_error()
+
+
+def test_last_error_is_per_thread(lib):
+    """Each host thread sees the text of its own last failing call."""
+    import threading
+
+    results = {}
+    go = threading.Barrier(2)
+
+    def worker(name, kw, expect):
+        go.wait()
+        for _ in range(200):
+            st = fwd(**kw)
+            txt = _abi.fa_last_error()
+            if st == _abi.FA_OK or expect not in txt:
+                results[name] = txt
+                return
+        results[name] = "ok"
+
+    a = threading.Thread(target=worker, args=("a", dict(D=96), "head_dim 96"))
+    b = threading.Thread(target=worker, args=("b", dict(Hq=3, Hkv=2), "not a multiple"))
+    a.start(); b.start(); a.join(); b.join()
+    assert results == {"a": "ok", "b": "ok"}, results
