@@ -30,9 +30,12 @@
 //     of the dO tile) and hands P to its partner through LDS; the partner
 //     computes dP = dO V^T, then dS and dK^T += Q^T dS.  Each wave so holds
 //     one accumulator and one operand.  The group's query heads add into the
-//     same accumulators, so GQA needs no reduction pass.
-// Masks (causal, sliding window, the key count) are those of the forward;
-// tiles a wave's rows cannot see are skipped, partly visible ones are masked.
+//     same accumulators, so GQA needs no reduction pass.  (At D = 256: 4 waves,
+//     64 keys, one wave per SIMD.)
+// The gradients are staged through LDS and written as whole rows with
+// non-temporal stores.  Masks (causal, sliding window, the key count) and
+// packed sequences (cumulative offsets) are those of the forward; tiles a
+// wave's rows cannot see are skipped, partly visible ones are masked.
 #include <type_traits>
 
 #include "fa_common.hpp"

@@ -13,8 +13,9 @@
 //
 // gfx950 mapping (one workgroup = 4 wave64 = 128 query rows):
 //   * K and V tiles of BN keys stream HBM -> LDS with global_load_lds_dwordx4
-//     (no VGPR round trip), double-buffered: the copy of tile t+1 runs while
-//     tile t is computed; one barrier per tile.  Rows are stored row-major
+//     (no VGPR round trip), double-buffered, K one tile ahead of V: while
+//     tile t's probabilities are formed, S of tile t+1 is computed; one
+//     barrier per tile.  Rows are stored row-major
 //     with their 16-byte chunks XOR-swizzled by row so that the MFMA operand
 //     reads below hit distinct LDS banks.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: A = K rows from LDS
@@ -32,7 +33,8 @@
 //     ("5 years, 10K stars: xformers", cloud.tencent.com) are read this way.
 //     KV tiles no row of the workgroup sees are never loaded; tiles every row
 //     sees whole run a mask-free main loop, the few others a masked one.
-//     Workgroups are issued heaviest query tile first.
+//     Workgroups are issued heaviest query tile first within XCD-sized
+//     windows of heads (xcd_work_item).
 //   * Block-diagonal packing: with cumulative offsets cu_q / cu_k, sequence b
 //     is rows cu_q[b] .. cu_q[b+1]-1 of Q/O (cu_k for K/V) and attends only to
 //     itself; without them the batch is dense [B, L, H, D].
@@ -42,7 +44,8 @@
 //     bf16/fp16 range, and O = acc / l and lse = m_ref + log(l) are unchanged
 //     up to rounding.
 //   * The output tile is staged through LDS so each row is written to HBM as
-//     full contiguous 16-byte-per-lane stores.
+//     full contiguous 16-byte-per-lane stores, non-temporal (O is not read
+//     back here).
 #include <type_traits>
 
 #include "fa_common.hpp"
