@@ -38,11 +38,16 @@
 //   * Block-diagonal packing: with cumulative offsets cu_q / cu_k, sequence b
 //     is rows cu_q[b] .. cu_q[b+1]-1 of Q/O (cu_k for K/V) and attends only to
 //     itself; without them the batch is dense [B, L, H, D].
-//   * Lazy rescaling: a row's reference max moves only when a new score
-//     exceeds it by more than 2^8 in the exponent, so the accumulator rescale
-//     (D/2 multiplies per lane) is rare; probabilities stay <= 256, inside
-//     bf16/fp16 range, and O = acc / l and lse = m_ref + log(l) are unchanged
-//     up to rounding.
+//   * Lazy rescaling: probabilities are formed against a row's reference max
+//     m_ref and the tile is accepted while each lane's share of the tile's
+//     probabilities sums to at most 2^8 (so none exceeds 2^8, inside bf16/fp16
+//     range).  Only otherwise -- the row's first visible tile, or scores a few
+//     units above m_ref -- is the tile's row max taken, the accumulator
+//     rescaled and the probabilities formed again.  The common step thus
+//     computes no row max at all; O = acc / l and lse = m_ref + log(l) are
+//     unchanged up to rounding.
+//   * In the main phase the tile copies advance a running pointer with no
+//     bounds clamping (every tile there is whole).
 //   * The output tile is staged through LDS so each row is written to HBM as
 //     full contiguous 16-byte-per-lane stores, non-temporal (O is not read
 //     back here).
@@ -100,7 +105,7 @@ struct FwdParams {
   int Lq, Lk;       // dense: sequence lengths; packed: the longest ones
   int total_q, total_k;
   int win_left, win_right;  // < 0: unbounded
-  float scale2, thr;
+  float scale2;
   uint32_t qxor;
   int xcd_w;  // work-list window, see xcd_work_item
 };
@@ -109,7 +114,7 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kNT, (D <= 128 ? 2 : 1))
 void fwd_kernel(const FwdParams prm) {
   const int B = prm.B, Hq = prm.Hq, Hkv = prm.Hkv;
-  const float scale2 = prm.scale2, thr = prm.thr;
+  const float scale2 = prm.scale2;
   const uint32_t qxor = prm.qxor;
   constexpr int BM = kFwdBM;
   constexpr int BN = FwdTile<D>::BN;
@@ -225,6 +230,15 @@ void fwd_kernel(const FwdParams prm) {
         load_lds16_off(base, clamp_off(i, j0, ld[i]), dst + (i * kFwdWaves + wu) * 512);
     }
   };
+  // Main-phase copies: the tile is whole and inside the sequence, no clamping;
+  // `base` is a running wave-uniform pointer to the tile's first row.
+  auto issue_whole = [&](const uint16_t* base, const uint32_t (&ld)[NLOAD], uint16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * kFwdWaves + wu) * 512);
+  };
+  const long tstride = (long)BN * kstride;
+  const uint16_t* kp = Kb;
+  const uint16_t* vp = Vb;
   auto issue_k = [&](int u, uint16_t* dK) { issue(Kb, ldk, t_first + u, dK); };
   auto issue_v = [&](int u, uint16_t* dV) { issue(Vb, ldv, t_first + u, dV); };
   // Q^T operand: lane holds query `qrow`, 8 dims per 16-dim k-step.
@@ -280,14 +294,11 @@ void fwd_kernel(const FwdParams prm) {
     }
   };
 
-  // Folds tile t's row max into the reference max and rescales the
-  // accumulator if it moved.  With MASK, first sets the scores of keys the row
-  // may not see to -inf (only tiles crossing the diagonal or the key tail).
-  auto fold = [&](f32x16 (&s)[BN / 32], int u, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // Sets the scores of keys the row may not see to -inf (only tiles crossing
+  // the diagonal, a window edge or the key tail).
+  auto mask = [&](f32x16 (&s)[BN / 32], int u) {
     const int j0 = (t_first + u) * BN;
-    float mx = -INFINITY;
-    if (MASK && (j0 < kmin(qw_last) || j0 + BN - 1 > kmax(qw0))) {
+    if (j0 < kmin(qw_last) || j0 + BN - 1 > kmax(qw0)) {
       // key j0 + 32kb + 8(r/4) + 4hf + r%4 is visible iff it is in [row_kmin, row_kmax]
       const int hi = row_kmax - j0 - 4 * hf, lo = row_kmin - j0 - 4 * hf;
 #pragma unroll
@@ -296,36 +307,18 @@ void fwd_kernel(const FwdParams prm) {
         for (int r = 0; r < 16; ++r) {
           const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
           if (off > hi || off < lo) s[kb][r] = -INFINITY;
-          mx = fmaxf(mx, s[kb][r]);
         }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    }
-    mx = max_halves(mx);
-    const bool upd = mx > m_ref + thr;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(upd) != 0, 0)) {
-      // Rare: keep it a real branch (the marker stops it being turned into
-      // unconditional multiplies of the whole accumulator).
-      asm volatile("" ::: "memory");
-      const float m_new = upd ? mx : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast((m_ref - m_new) * scale2);
-      l_part *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-      m_ref = m_new;
     }
   };
 
-  // P = exp2(s*scale2 - m*scale2) for a folded tile, rounded to T and packed
+  // P = exp2(s*scale2 - m_ref*scale2) for a masked tile, rounded to T and packed
   // as the B operand of the PV MFMA.  Masked scores are -inf and give exactly
   // 0 (scale2 > 0, mb finite).  The row sum adds the unrounded fp32 values,
   // so lse carries no 16-bit rounding (summing the rounded values would shift
   // ln(l) by up to 2^-9 for rows with few keys).
-  auto make_p = [&](const f32x16 (&s)[BN / 32], uint32_t (&pk)[BN / 32][8]) {
+  auto exp_pack = [&](const f32x16 (&s)[BN / 32], uint32_t (&pk)[BN / 32][8]) {
     const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * scale2;
+    float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -333,8 +326,36 @@ void fwd_kernel(const FwdParams prm) {
         const float p0 = exp2_fast(__builtin_fmaf(s[kb][2 * j], scale2, -mb));
         const float p1 = exp2_fast(__builtin_fmaf(s[kb][2 * j + 1], scale2, -mb));
         pk[kb][j] = Ops<T>::pack2(p0, p1);
-        l_part += p0 + p1;
+        ls += p0 + p1;
       }
+    return ls;
+  };
+  // The reference max moves lazily: a tile is accepted as long as this lane's
+  // probabilities sum to at most 2^8 (so each is <= 2^8).  Otherwise (a score
+  // more than a few units above the reference, the first visible tile, or a
+  // NaN) the tile's row max is folded in, the accumulator rescaled and the
+  // probabilities recomputed.
+  auto make_p = [&](const f32x16 (&s)[BN / 32], uint32_t (&pk)[BN / 32][8]) {
+    float ls = exp_pack(s, pk);
+    const bool bad = !(ls <= 256.f) || m_ref == -INFINITY;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
+      asm volatile("" ::: "memory");
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max_halves(mx);
+      if (mx > m_ref) {
+        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast((m_ref - mx) * scale2);
+        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        m_ref = mx;
+      }
+      ls = exp_pack(s, pk);
+    }
+    l_part += ls;
   };
   // O^T += V^T P^T, 16 keys per MFMA k-step (slots 4r+k <-> key 16t+8r+4hf+k).
   auto pv = [&](const uint32_t (&pk)[BN / 32][8], const uint16_t* sV) {
@@ -366,33 +387,42 @@ void fwd_kernel(const FwdParams prm) {
   };
   auto clampt = [&](int t) { return min(t, ntiles - 1); };
 
-  // One pipeline step for tile t: its scores sc are folded already, K(t+1)
+  // One pipeline step for tile t: its scores sc are masked already, K(t+1)
   // and V(t) have been requested kStages-1 steps ago.  Refills the stages of
-  // K(t) and V(t-1) with K(t+kStages) and V(t+kStages-1), then computes P(t),
-  // S(t+1) and P(t) V(t).  In the main phase (TAIL false) tiles t and t+1 are
-  // fully visible to every row of the workgroup, so nothing is masked or
-  // skipped.
+  // K(t) and V(t-1) with K(t+kStages) and V(t+kStages-1), then computes
+  // S(t+1), P(t) and P(t) V(t) (S first, so its MFMAs overlap the exponentials;
+  // the acceptance test of P(t) comes before the PV MFMAs that read it).  In
+  // the main phase (TAIL false) tiles t and t+1 are fully visible to every row
+  // of the workgroup, so nothing is masked or skipped.
   auto step = [&](int t, auto I, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32], auto tail_tag) {
     constexpr int i = decltype(I)::value;
     constexpr bool TAIL = decltype(tail_tag)::value;
     using Inext = std::integral_constant<int, (i + 1) % kStages>;
     using Iprev = std::integral_constant<int, (i + kStages - 1) % kStages>;
     tile_wait_barrier(std::integral_constant<int, (kStages - 2) * kPerTile>{});
-    issue_k(clampt(t + kStages), kst(I));
-    issue_v(clampt(t + kStages - 1), vst(Iprev{}));
+    if (TAIL) {
+      issue_k(clampt(t + kStages), kst(I));
+      issue_v(clampt(t + kStages - 1), vst(Iprev{}));
+    } else {
+      issue_whole(kp, ldk, kst(I));
+      issue_whole(vp, ldv, vst(Iprev{}));
+      kp += tstride;
+      vp += tstride;
+    }
     if (TAIL && (t > last_live || t + 1 < first_live)) return;  // tile t and t+1 hidden from this wave
     if (TAIL && t + 1 == first_live) {  // tile t hidden, t+1 the wave's first
       scores(sn, kst(Inext{}));
-      fold(sn, t + 1, std::integral_constant<bool, true>{});
+      mask(sn, t + 1);
       return;
     }
     uint32_t pk[BN / 32][8];
-    make_p(sc, pk);
     if (!TAIL || t + 1 <= last_live) {
       scores(sn, kst(Inext{}));
+      make_p(sc, pk);
       pv(pk, vst(I));
-      fold(sn, t + 1, std::integral_constant<bool, TAIL>{});
+      if (TAIL) mask(sn, t + 1);
     } else {
+      make_p(sc, pk);
       pv(pk, vst(I));
     }
   };
@@ -422,7 +452,7 @@ void fwd_kernel(const FwdParams prm) {
     tile_wait_barrier(std::integral_constant<int, (kStages - 1) * kPerTile>{});  // K(0) landed
     if (first_live == 0 && last_live >= 0) {
       scores(sA, sK0);
-      fold(sA, 0, Tail{});
+      mask(sA, 0);
     }
     // Every phase walks kStages tiles at a time from t = 0, so stages and
     // score arrays are in the same roles at every loop head.
@@ -443,6 +473,8 @@ void fwd_kernel(const FwdParams prm) {
       t += kStages;
     }
     // Main phase: step t runs unmasked when tiles t and t+1 are both whole.
+    kp = Kb + (long)(t_first + t + kStages) * tstride;
+    vp = Vb + (long)(t_first + t + kStages - 1) * tstride;
     while (t >= m_lo && t + kStages < m_hi) {
       step(t, S0{}, sA, sB, Main{});
       step(t + 1, S1{}, sB, sA, Main{});
@@ -527,8 +559,6 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   // |scale| * log2(e), kept >= 1e-30 so that masked (-inf) scores always give
   // probability 0; for scale 0 this changes no result beyond 1e-30 relative.
   p.scale2 = fmaxf(fabsf(s) * kLog2e, 1e-30f);
-  // Rescale threshold of 8 (log2 units) expressed in raw score units.
-  p.thr = 8.f / p.scale2;
   p.qxor = (s < 0.f) ? 0x80008000u : 0u;
   // blocks resident per CU at this kernel's register use: 3 (D=64), 2, 1 (D=256)
   p.xcd_w = xcd_window(a.B, a.Hq, a.Hkv, nqt, D == 64 ? 3 : D == 128 ? 2 : 1);

@@ -60,6 +60,29 @@ def test_large_logits(gpu):
     check(1, 700, 700, 2, 2, 128, torch.bfloat16, True, seed=79, gpu=gpu, q_scale=8.0)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("direction", [1.0, -1.0], ids=["rising", "falling"])
+def test_steadily_moving_scores(direction, causal, gpu):
+    """Scores along the keys rise (or fall) by about 2 in log2 units every 32
+    keys, about 60 over the row: rising, a row's reference max is overtaken
+    again and again, so the accept-or-rescale test fires on many tiles;
+    falling, the first tile already holds the maximum."""
+    B, L, H, D = 1, 1000, 2, 128
+    q, k, v = W.randn_qkv(B, L, L, H, H, D, torch.float32, 93)
+    u = torch.randn(D, generator=torch.Generator().manual_seed(94))
+    u = u / u.norm()
+    ramp = direction * torch.arange(L, dtype=torch.float32) / L
+    q = (16.0 * u + 0.5 * q).to(torch.bfloat16)
+    k = (29.4 * ramp[None, :, None, None] * u + 0.5 * k).to(torch.bfloat16)
+    v = v.to(torch.bfloat16)
+    scale = f32(D ** -0.5)
+    tag = f"moving scores direction={direction} causal={causal}"
+    say(f"case {tag}")
+    o, lse = run(q, k, v, scale, causal, gpu)
+    o_ref, l_ref = oracle.attention_ref(q, k, v, scale, causal)
+    compare(o, lse, o_ref, l_ref, tag)
+
+
 @pytest.mark.parametrize("name", ["tiny", "encoder"])
 def test_config_full(name, gpu):
     cfg = W.PREFILL[name]
