@@ -17,7 +17,9 @@
 //     keys (16h .. 16h+15 of the block).
 //   * O^T += V^T P^T: one MFMA (k = 64 keys) per 32 head dimensions.  B =
 //     P^T straight from the score registers, scaled by 256 (so the e4m3
-//     rounding stays clear of subnormals) and packed with v_cvt_pk_fp8_f32;
+//     rounding stays clear of subnormals; the factor is added as 8 to the
+//     exponent and removed through the row sum) and packed with
+//     v_cvt_pk_fp8_f32;
 //     A = 32 bytes of one V^T row (two ds_read_b128 of keys 16h.. and
 //     32+16h..), matching the keys each lane's P bytes carry.  The two
 //     operands of the f8f6f4 MFMA share their k layout, so matching byte
@@ -52,7 +54,7 @@ struct Fp8Params {
   int win_left, win_right;
   float scale2;  // |scale * q_descale * k_descale| * log2(e)
   float thr;     // lazy-rescale slack in raw score units
-  float oscale;  // v_descale / 256
+  float oscale;  // v_descale
   uint32_t qxor; // sign flip of q for a negative scale
   int xcd_w;     // work-list window, see xcd_work_item
 };
@@ -153,9 +155,12 @@ void fwd_fp8_kernel(const Fp8Params prm) {
     const int d = P >> 2, pc = P & 3;
     voff[i] = (uint32_t)(d * prm.vt_stride + 16 * (pc ^ swz_v8(d)));
   }
+  // Tiles are requested in order, so the K tile pointer advances by one
+  // tile's rows per request.
+  const long ktile = (long)kPBN * kstride;
+  const uint8_t* kbase = Kb + (long)t_first * ktile;
   auto issue = [&](int t, uint8_t* dK, uint8_t* dV) {
     const int j0 = t * kPBN;
-    const uint8_t* kbase = Kb + (long)j0 * kstride;
     const bool whole = j0 + kPBN <= Lk;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
@@ -166,6 +171,7 @@ void fwd_fp8_kernel(const Fp8Params prm) {
     // V^T columns j0 .. j0+63 lie inside the row (stride a multiple of 64 >= Lk)
 #pragma unroll
     for (int i = 0; i < NV; ++i) load_lds16_off(Vb + j0, voff[i], dV + (i * kPW + wu) * 1024);
+    kbase += ktile;
   };
 
   // A-operand rows of the S^T MFMA: lane i reads K row 16((i/4)%2) + 4(i/8) + i%4.
@@ -217,9 +223,11 @@ void fwd_fp8_kernel(const Fp8Params prm) {
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       m_ref = m_new;
     }
-    // P (x256 for the e4m3 rounding), packed four keys per dword: dword j of
-    // the B operand carries keys 16(j/4)... i.e. block j/4, elements 4(j%4)..+3.
-    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * scale2;
+    // 256 P (the factor keeps the e4m3 rounding clear of subnormals; it enters
+    // as +8 in the exponent and leaves through the row sum), packed four keys
+    // per dword: dword j of the B operand carries keys 16(j/4)... i.e. block
+    // j/4, elements 4(j%4)..+3.
+    const float mb = ((m_ref == -INFINITY) ? 0.f : m_ref * scale2) - 8.f;
     i32x8 pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -230,8 +238,8 @@ void fwd_fp8_kernel(const Fp8Params prm) {
         p[t] = exp2_fast(__builtin_fmaf(s[kb][r0 + t], scale2, -mb));
         l_part += p[t];
       }
-      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.f, p[1] * 256.f, 0, false);
-      wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.f, p[3] * 256.f, wd, true);
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
       pb[j] = wd;
     }
     // O^T += V^T P^T: A = V^T row d, keys 16hf .. +15 and 32+16hf .. +15
@@ -293,7 +301,7 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   }
   if (hf == 0 && qrow < Lq)
     __builtin_nontemporal_store(
-        l > 0.f ? (m_ref * scale2 + __builtin_log2f(l)) * kLn2 : -INFINITY,
+        l > 0.f ? (m_ref * scale2 + __builtin_log2f(l) - 8.f) * kLn2 : -INFINITY,
         prm.LSE + ((long)b * Hq + h) * Lq + qrow);
 }
 
@@ -316,7 +324,7 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
   const float sc = a.scale * a.q_descale * a.k_descale;
   p.scale2 = fmaxf(fabsf(sc) * kLog2e, 1e-30f);
   p.thr = 0.5f / p.scale2;
-  p.oscale = a.v_descale / 256.f;
+  p.oscale = a.v_descale;
   p.qxor = sc < 0.f ? 0x80808080u : 0u;
   const int nqt = (a.Lq + kPBM - 1) / kPBM;
   // blocks resident per CU at this kernel's register use: 4 (D=64), 3 (D=128)
