@@ -14,7 +14,8 @@
 // Three kernels, none of them with atomics (results are bitwise
 // reproducible):
 //   * prep: D_i and lse_i * log2(e) per row into a workspace (+inf for rows
-//     that see no key, so their probabilities come out 0).
+//     that see no key and for the padding rows past a sequence's end, whose
+//     D is 0, so their probabilities and dS come out exactly 0).
 //   * dq (query-major, like the forward): a workgroup owns 128 query rows (32
 //     per wave, one per lane column) and streams K/V tiles of 32 keys through
 //     LDS (LDS-direct copies, two stages).  Per tile and wave:
@@ -35,7 +36,9 @@
 // The gradients are staged through LDS and written as whole rows with
 // non-temporal stores.  Masks (causal, sliding window, the key count) and
 // packed sequences (cumulative offsets) are those of the forward; tiles a
-// wave's rows cannot see are skipped, partly visible ones are masked.
+// wave's rows cannot see are skipped, partly visible ones are masked by
+// setting the hidden scores to -inf in a wave-uniform branch, so P and dS are
+// then formed with no per-element select.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -60,8 +63,8 @@ struct BwdParams {
   uint16_t* dQ;
   uint16_t* dK;
   uint16_t* dV;
-  float* lse2;  // workspace [B, Hq, Lqp]: lse * log2(e), +inf for rows with no key
-  float* Dd;    // workspace [B, Hq, Lqp]: rowsum(dO * O)
+  float* lse2;  // workspace [B, Hq, Lqp]: lse * log2(e), +inf for rows with no key and padding rows
+  float* Dd;    // workspace [B, Hq, Lqp]: rowsum(dO * O), 0 for padding rows
   const int* cu_q;  // packed sequences: offsets [B + 1] into the rows, or nullptr
   const int* cu_k;
   int total_q, total_k;  // packed row counts
@@ -97,21 +100,24 @@ __device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b) {
 
 // Per-row statistics: D_i = dO_i . O_i and lse_i * log2(e).  CPR lanes (one
 // 16-byte chunk each) per (row, head); rows in memory order [B, Lq, Hq].
+// The workspace rows past a sequence's end (up to the padded length Lqp) get
+// lse2 = +inf and D = 0, so that they give P = 0 and dS = 0 exactly.
 template <typename T, int D>
 __global__ __launch_bounds__(256)
 void bwd_prep_kernel(const BwdParams p) {
   constexpr int CPR = D / 8;
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gid / CPR;  // (b * Lq + i) * Hq + h; packed: Lq is the longest length
+  const long row = gid / CPR;  // (b * Lqp + i) * Hq + h; packed: Lqp pads the longest length
   const int c = (int)(gid % CPR);
-  const long nrows = (long)p.B * p.Lq * p.Hq;
+  const long nrows = (long)p.B * p.Lqp * p.Hq;
   const int h = (int)(row % p.Hq);
   const long bi = row / p.Hq;
-  const int i = (int)(bi % p.Lq);
-  const int b = (int)(bi / p.Lq);
-  bool valid = row < nrows;
+  const int i = (int)(bi % p.Lqp);
+  const int b = (int)(bi / p.Lqp);
+  const bool inrange = row < nrows;
+  bool valid = false;
   SeqRows sr{0, 0, 0, 0};
-  if (valid) {
+  if (inrange) {
     sr = seq_rows(p, b);
     valid = i < sr.Lq;
   }
@@ -127,13 +133,18 @@ void bwd_prep_kernel(const BwdParams p) {
   }
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (valid && c == 0) {
+  if (inrange && c == 0) {
     const long oi = ((long)b * p.Hq + h) * p.Lqp + i;
-    // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
-    const long li = p.cu_q ? (long)h * p.total_q + sr.qs + i : ((long)b * p.Hq + h) * p.Lq + i;
-    const float l = p.LSE[li];
-    p.Dd[oi] = acc;
-    p.lse2[oi] = l == -INFINITY ? INFINITY : l * kLog2e;
+    if (valid) {
+      // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
+      const long li = p.cu_q ? (long)h * p.total_q + sr.qs + i : ((long)b * p.Hq + h) * p.Lq + i;
+      const float l = p.LSE[li];
+      p.Dd[oi] = acc;
+      p.lse2[oi] = l == -INFINITY ? INFINITY : l * kLog2e;
+    } else {
+      p.Dd[oi] = 0.f;
+      p.lse2[oi] = INFINITY;
+    }
   }
 }
 
@@ -356,9 +367,17 @@ void bwd_dq_kernel(const BwdParams p) {
       s = Ops<T>::mfma32(ld_row_chunk<D>(sK, l32, 2 * kk + hf), qf[kk], s);
       dp = Ops<T>::mfma32(ld_row_chunk<D>(sV, l32, 2 * kk + hf), df[kk], dp);
     }
-    // key j0 + 8(r/4) + 4hf + r%4 of query qrow: visible iff in [row_kmin, row_kmax]
-    const bool whole = j0 >= kmin(qw_last) && j0 + BN - 1 <= kmax(qw0) && qw0 + kBR <= Lq;
-    const int lo = row_kmin - j0 - 4 * hf, hi = row_kmax - j0 - 4 * hf;
+    // key j0 + 8(r/4) + 4hf + r%4 of query qrow: visible iff in [row_kmin,
+    // row_kmax]; hidden scores become -inf, so P and dS are exactly 0 there
+    // (rows past the end have lse2 = +inf and D = 0: also P = dS = 0).
+    if (!(j0 >= kmin(qw_last) && j0 + BN - 1 <= kmax(qw0))) {
+      const int lo = row_kmin - j0 - 4 * hf, hi = row_kmax - j0 - 4 * hf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off < lo || off > hi) s[r] = -INFINITY;
+      }
+    }
     uint32_t dsk[8];
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -366,10 +385,8 @@ void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * jj + e;
-        const int off = 8 * (r >> 2) + (r & 3);
         const float pr = exp2_fast(__builtin_fmaf(s[r], scale2, -lse2));
-        const float ds = pr * (dp[r] - Dq);
-        d2[e] = (whole || (off >= lo && off <= hi)) ? ds : 0.f;
+        d2[e] = pr * (dp[r] - Dq);
       }
       dsk[jj] = Ops<T>::pack2(d2[0], d2[1]);
     }
@@ -541,13 +558,15 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int kstride = Hkv * D;
   const int qstride = Hq * D;
   // This wave's operand: K^T (P wave) or V^T (dS wave); lane holds key `key`
-  // (clamped), 8 dims per k-step.
+  // (clamped), 8 dims per k-step.  For a negative scale the P wave flips the
+  // sign of K (S = Q (-K)^T, the same as flipping Q).
   u32x4 kv[D / 16];
   {
     const long krow = ((long)sr.ks + min(key, Lk - 1)) * kstride + (long)kvh * D;
     const uint16_t* src = sw ? p.V : p.K;
+    const uint32_t kx = sw ? 0u : p.qxor;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) kv[s] = load16(src + krow + 16 * s + 8 * hf);
+    for (int s = 0; s < D / 16; ++s) kv[s] = load16(src + krow + 16 * s + 8 * hf) ^ kx;
   }
 
   const int i_lo = qlo(k0), i_hi = qhi(k_last);
@@ -558,10 +577,9 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int first_live = pair_live ? wi_lo / BQ - s_first : nsteps;
   const int last_live = pair_live ? wi_hi / BQ - s_first : -1;
   const int ntiles = g * nsteps;  // (query head of the group, query step) pairs
-  auto live = [&](int u) {
-    const int st = u % nsteps;
-    return st >= first_live && st <= last_live;
-  };
+  // Tile u is query step u % nsteps of query head u / nsteps of the group;
+  // the loop keeps these for tiles u - 1, u and u + 1 as running counters.
+  auto live_st = [&](int st) { return st >= first_live && st <= last_live; };
 
   PairTileLoader<D, BQ> ldr;
   ldr.init(wu, lane, qstride);
@@ -569,9 +587,9 @@ void bwd_dkdv_kernel(const BwdParams p) {
   tr_offsets<D>(lane, toff);
 
   // lse2 / D copy: wave 0, lanes 0..15 (8 chunks of 4 rows each).
-  auto issue_tile = [&](int u, uint16_t* dq_tile, uint16_t* dg_tile, float* dl) __attribute__((always_inline)) {
-    const int hh = kvh * g + u / nsteps;
-    const int q0 = (s_first + u % nsteps) * BQ;
+  auto issue_tile = [&](int hg, int st, uint16_t* dq_tile, uint16_t* dg_tile, float* dl) __attribute__((always_inline)) {
+    const int hh = kvh * g + hg;
+    const int q0 = (s_first + st) * BQ;
     const long hbase = (long)sr.qs * qstride + (long)hh * D;
     ldr.issue(p.Q + hbase, p.dO + hbase, q0, Lq - 1, qstride, wu, dq_tile, dg_tile);
     if (wu == 0 && lane < 16) {
@@ -586,19 +604,25 @@ void bwd_dkdv_kernel(const BwdParams p) {
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
   f32x16 dp = (f32x16){};  // dS wave: dP of the previous step's tile
   const float scale2 = p.scale2;
-  const uint32_t qxor = p.qxor;
 
   // P wave, tile u: S, P (stored for the partner), dV^T += dO^T P.
-  auto p_tile = [&](int u, const uint16_t* sQ, const uint16_t* sG, const float* sL) __attribute__((always_inline)) {
-    const int q0 = (s_first + u % nsteps) * BQ;
+  auto p_tile = [&](int u, int st, const uint16_t* sQ, const uint16_t* sG, const float* sL) __attribute__((always_inline)) {
+    const int q0 = (s_first + st) * BQ;
     f32x16 s = (f32x16){};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
-      s = Ops<T>::mfma32(ld_row_chunk<D>(sQ, l32, 2 * kk + hf) ^ qxor, kv[kk], s);
-    // element r: query q0 + 8(r/4) + 4hf + r%4, key `key`
+      s = Ops<T>::mfma32(ld_row_chunk<D>(sQ, l32, 2 * kk + hf), kv[kk], s);
+    // element r: query q0 + 8(r/4) + 4hf + r%4, key `key`.  Scores the rows
+    // may not see become -inf, so P is exactly 0 there (rows past the end
+    // have lse2 = +inf: P = 0 as well).
     const int qlast = min(q0 + BQ, Lq) - 1;
-    const bool whole = q0 + BQ <= Lq && kw0 >= kmin(qlast) && kw0 + kBR - 1 <= kmax(q0) &&
-                       kw0 + kBR <= Lk;
+    if (!(kw0 >= kmin(qlast) && kw0 + kBR - 1 <= kmax(q0) && kw0 + kBR <= Lk)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key < kmin(qi) || key > kmax(qi)) s[r] = -INFINITY;
+      }
+    }
     float* xs = &sX[u & 1][pair][0];
     uint32_t pk[8];
 #pragma unroll
@@ -606,12 +630,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
       const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 8 * gq + 4 * hf);
       f32x4 pr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = q0 + 8 * gq + 4 * hf + i;
-        const bool vis = whole || (qi < Lq && key >= kmin(qi) && key <= kmax(qi));
-        const float e = exp2_fast(__builtin_fmaf(s[4 * gq + i], scale2, -L4[i]));
-        pr[i] = vis ? e : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(__builtin_fmaf(s[4 * gq + i], scale2, -L4[i]));
       *reinterpret_cast<f32x4*>(xs + 4 * (gq * 64 + lane)) = pr;
       pk[2 * gq] = Ops<T>::pack2(pr[0], pr[1]);
       pk[2 * gq + 1] = Ops<T>::pack2(pr[2], pr[3]);
@@ -632,8 +651,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
       dp = Ops<T>::mfma32(ld_row_chunk<D>(sG, l32, 2 * kk + hf), kv[kk], dp);
   };
   // dS wave, tile u (one step later): dS = P (dP - D), dK^T += Q^T dS.
-  // Entries the rows may not see have P = 0 and give dS = 0 (the test on P
-  // also keeps the unset D of padding rows out).
+  // Entries the rows may not see have P = 0 and give dS = 0 (padding rows
+  // have D = 0).
   auto ds_tile = [&](int u, const uint16_t* sQ, const float* sL) __attribute__((always_inline)) {
     const float* xs = &sX[u & 1][pair][0];
     uint32_t dsk[8];
@@ -643,7 +662,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
       const f32x4 pr = *reinterpret_cast<const f32x4*>(xs + 4 * (gq * 64 + lane));
       float ds[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ds[i] = pr[i] != 0.f ? pr[i] * (dp[4 * gq + i] - D4[i]) : 0.f;
+      for (int i = 0; i < 4; ++i) ds[i] = pr[i] * (dp[4 * gq + i] - D4[i]);
       dsk[2 * gq] = Ops<T>::pack2(ds[0], ds[1]);
       dsk[2 * gq + 1] = Ops<T>::pack2(ds[2], ds[3]);
     }
@@ -661,17 +680,26 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // copies of tile u + 1 are issued and the pair works on tiles u and u - 1.
   // The two kinds of wave run separate loops (so their registers are not
   // allocated side by side) with the same barriers.
+  // Query step of tiles u - 1, u, u + 1 and query head (within the group) of
+  // tile u + 1.
+  int st_prev = 0, st_cur = 0, st_next = nsteps > 1 ? 1 : 0, hg_next = nsteps > 1 ? 0 : 1;
   auto step = [&](int u, auto I, auto role) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
     using Inext = std::integral_constant<int, (i + 1) % 3>;
     using Iprev = std::integral_constant<int, (i + 2) % 3>;
     copies_done_barrier();
-    if (u + 1 < ntiles) issue_tile(u + 1, qst(Inext{}), gst(Inext{}), lst(Inext{}));
+    if (u + 1 < ntiles) issue_tile(hg_next, st_next, qst(Inext{}), gst(Inext{}), lst(Inext{}));
     if constexpr (!decltype(role)::value) {
-      if (u < ntiles && live(u)) p_tile(u, qst(I), gst(I), lst(I));
+      if (u < ntiles && live_st(st_cur)) p_tile(u, st_cur, qst(I), gst(I), lst(I));
     } else {
-      if (u >= 1 && live(u - 1)) ds_tile(u - 1, qst(Iprev{}), lst(Iprev{}));
-      if (u < ntiles && live(u)) dp_tile(gst(I));
+      if (u >= 1 && live_st(st_prev)) ds_tile(u - 1, qst(Iprev{}), lst(Iprev{}));
+      if (u < ntiles && live_st(st_cur)) dp_tile(gst(I));
+    }
+    st_prev = st_cur;
+    st_cur = st_next;
+    if (++st_next == nsteps) {
+      st_next = 0;
+      ++hg_next;
     }
   };
   auto run = [&](auto role) __attribute__((always_inline)) {
@@ -689,7 +717,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   };
 
   if (ntiles > 0) {
-    issue_tile(0, sQ0, sG0, sL0);
+    issue_tile(0, 0, sQ0, sG0, sL0);
     if (sw)
       run(std::true_type{});
     else
@@ -736,7 +764,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.qxor = a.scale < 0.f ? 0x80008000u : 0u;
 
-  const long nrows = (long)a.B * a.Lq * a.Hq;
+  const long nrows = (long)a.B * p.Lqp * a.Hq;
   const long nthreads = nrows * (D / 8);
   hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
                      stream, p);

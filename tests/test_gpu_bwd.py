@@ -135,6 +135,44 @@ def test_bwd_deterministic(gpu):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["dense", "packed"])
+def test_bwd_ignores_workspace_contents(packed, gpu):
+    """The gradients do not depend on what the workspace held before the
+    call: a workspace filled with NaN gives bit-identical results to a zeroed
+    one (the padding rows past each sequence's end included)."""
+    from exact_tiled_attention_fa_amd import _abi
+    from exact_tiled_attention_fa_amd.attention import (flash_attn_bwd, flash_attn_fwd,
+                                                        flash_attn_varlen, flash_attn_varlen_bwd)
+
+    D, Hq, Hkv = 128, 4, 2
+    q, k, v = W.randn_qkv(1, 277, 277, Hq, Hkv, D, torch.bfloat16, 18)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(19)).to(torch.bfloat16)
+    q, k, v, do = (t.to(gpu) for t in (q, k, v, do))
+    scale = f32(D ** -0.5)
+    outs = []
+    for fill in (0.0, float("nan")):
+        if packed:
+            cu = torch.tensor([0, 45, 45, 200, 277], dtype=torch.int32, device=gpu)
+            args = (q[0], k[0], v[0])
+            n = _abi.fa_bwd_workspace_size(4, Hq, 155)
+            ws = torch.full((n // 4,), fill, dtype=torch.float32, device=gpu)
+            o, lse = flash_attn_varlen(*args, cu, cu, 155, 155, softmax_scale=scale,
+                                       causal=True)
+            g = flash_attn_varlen_bwd(*args, o, lse, do[0], cu, cu, 155, 155,
+                                      softmax_scale=scale, causal=True, workspace=ws)
+        else:
+            n = _abi.fa_bwd_workspace_size(1, Hq, 277)
+            ws = torch.full((n // 4,), fill, dtype=torch.float32, device=gpu)
+            o, lse = flash_attn_fwd(q, k, v, softmax_scale=scale, causal=True)
+            g = flash_attn_bwd(q, k, v, o, lse, do, softmax_scale=scale, causal=True,
+                               workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in g])
+    for a, b in zip(*outs):
+        assert torch.isfinite(a.float()).all()
+        assert torch.equal(a, b)
+
+
 def test_bwd_full_size_sampled(gpu):
     """The Llama-2-7B-shaped causal workload (B=4, H=32, L=4096, D=128, bf16)
     in the launch the benchmark times; the oracle computes two whole K/V
