@@ -53,6 +53,23 @@ def test_decode_small(D, dtype, splits, gpu):
     assert torch.all(o[0] == 0) and torch.all(lse[0] == float("-inf"))  # empty cache
 
 
+@pytest.mark.parametrize("splits", [8, 64])
+def test_decode_long_cache(splits, gpu):
+    """A cache of 3 x 800000 rows x 8 K/V heads x 128 dims (2.5e9 elements):
+    the last sequence's 600000 rows lie past element 2^31 of the tensor.
+    Unused rows hold NaN, so a stray read shows."""
+    B, Hq, Hkv, D, lmax = 3, 32, 8, 128, 800000
+    lens = [5, 100, 600000]
+    q, kc, vc, lens_t = make_cache(B, Hq, Hkv, D, lens, lmax, torch.bfloat16, seed=96)
+    assert kc.numel() > 2 ** 31
+    scale = f32(D ** -0.5)
+    say(f"decode long cache {lens} splits={splits}")
+    o, lse = run(q, kc, vc, lens_t, scale, splits, gpu)
+    heads = [(b, h) for b in range(B) for h in (0, 13, 31)]
+    o_ref, l_ref = oracle.decode_ref(q, kc, vc, lens, scale, heads=heads)
+    compare(o, lse, o_ref, l_ref, f"long cache splits={splits}")
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (16, 2), (64, 2), (40, 8)])
 def test_decode_head_groups(Hq, Hkv, gpu):
     """Group sizes 1, 8, 32 (two 16-head groups) and 5 (ragged group)."""

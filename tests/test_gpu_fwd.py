@@ -109,6 +109,30 @@ def test_config_full_size_sampled(name, nheads, gpu):
     compare(o, lse, o_ref, l_ref, f"{name} heads={sorted(heads)}")
 
 
+def test_long_sequence_sampled_rows(gpu):
+    """Q and O of 147456 x 128 heads x 128 dims: 2.4e9 elements, so element
+    and byte offsets run past 2^31.  (Q repeats one random 16-head block over
+    the 8 head groups, each group on its own K/V head, which keeps the input
+    cheap to draw.)  In a causal prefill with Lq = Lk, query row i sees keys
+    0..i, which is one query against a cache of length i + 1: the oracle's
+    decode_ref gives that row exactly.  Rows at tile edges, the middle and
+    the end, in the first and the last heads."""
+    B, L, Hq, Hkv, D = 1, 147456, 128, 8, 128
+    gen = torch.Generator().manual_seed(95)
+    q = torch.randn((B, L, 16, D), generator=gen).to(torch.bfloat16).repeat(1, 1, Hq // 16, 1)
+    _, k, v = W.randn_qkv(B, 1, L, 1, Hkv, D, torch.bfloat16, 97)
+    assert q.numel() > 2 ** 31
+    scale = f32(D ** -0.5)
+    say(f"long causal prefill L={L} Hq={Hq} Hkv={Hkv} D={D}")
+    o, lse = run(q, k, v, scale, True, gpu)
+    heads = [0, 17, 120, 127]
+    sel = np.array(heads)
+    for i in [0, 1, 31, 32, 127, 128, 65537, 99999, L - 2, L - 1]:
+        o_ref, l_ref = oracle.decode_ref(q[:, i], k, v, [i + 1], scale,
+                                         heads=[(0, h) for h in heads])
+        compare(o[:, i][:, sel], lse[:, sel, i], o_ref[:, sel], l_ref[:, sel], f"row {i}")
+
+
 def test_causal_row0_is_exact(gpu):
     """Row 0 sees only key 0: P = 1 exactly, so O_0 = V[0] bit for bit and
     lse_0 = scale * q_0.k_0."""
