@@ -144,3 +144,49 @@ def test_random_decode_paged(case, gpu):
     o, lse = run(q, kp, vp, ks, vs, table, ln, scale, splits, gpu)
     o_ref, l_ref = oracle.decode_paged_ref(q, kp, vp, table, ln, scale, k_scales=ks, v_scales=vs)
     compare(o, lse, o_ref, l_ref, tag)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_forward_fp8(case, gpu):
+    """The FP8 forward over random shapes, head groups, D, causal, windows,
+    scales and output types, held to the FP8 tests' derived bound."""
+    from test_gpu_fp8 import check as fp8_check
+
+    rng = np.random.default_rng(5000 + case)
+    B = int(rng.integers(1, 3))
+    Lq, Lk = (int(x) for x in rng.integers(1, 500, 2))
+    Hq, Hkv = draw_heads(rng)
+    D = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    window = draw_window(rng)
+    scale = float(rng.uniform(-0.3, 0.3)) if rng.random() < 0.2 else None
+    out_dtype = DTYPES[int(rng.integers(0, 2))]
+    fp8_check(B, Lq, Lk, Hq, Hkv, D, causal, 6000 + case, gpu, window=window, scale=scale,
+              out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_decode(case, gpu):
+    """Split-KV decode over a dense cache: random batch, lengths (zero and
+    past the cache length included), head groups up to 32, D, dtypes, split
+    counts and scales; NaN in every cache row no sequence owns."""
+    from test_gpu_decode import make_cache
+    from test_gpu_decode import run as decode_run
+
+    rng = np.random.default_rng(7000 + case)
+    B = int(rng.integers(1, 6))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    Hq = Hkv * int(rng.choice([1, 4, 5, 16, 32]))
+    D = int(rng.choice([64, 128, 256]))
+    dtype = DTYPES[int(rng.integers(0, 2))]
+    lmax = int(rng.integers(1, 3000))
+    lens = [int(rng.integers(0, lmax + 40)) for _ in range(B)]
+    splits = int(rng.choice([1, 2, 3, 8, 16, 64]))
+    scale = f32(float(rng.uniform(-0.3, 0.3)) if rng.random() < 0.2 else D ** -0.5)
+    tag = (f"decode B={B} Hq={Hq} Hkv={Hkv} D={D} {str(dtype)[6:]} lmax={lmax} lens={lens} "
+           f"splits={splits} s={scale:.4g}")
+    say(tag)
+    q, kc, vc, lens_t = make_cache(B, Hq, Hkv, D, lens, lmax, dtype, seed=8000 + case)
+    o, lse = decode_run(q, kc, vc, lens_t, scale, splits, gpu)
+    o_ref, l_ref = oracle.decode_ref(q, kc, vc, lens, scale)
+    compare(o, lse, o_ref, l_ref, tag)
