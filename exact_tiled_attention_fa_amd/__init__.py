@@ -8,13 +8,14 @@ synthetic input generators.
 
 from . import _abi
 from ._abi import (fa_bwd, fa_bwd_ex, fa_bwd_workspace_size, fa_decode, fa_decode_paged,
-                   fa_decode_workspace_size, fa_fwd, fa_fwd_ex, fa_fwd_fp8, fa_info,
-                   fa_last_error)
+                   fa_decode_workspace_size, fa_fwd, fa_fwd_ex, fa_fwd_fp8, fa_fwd_fp8_ex,
+                   fa_info, fa_last_error)
 
 __all__ = [
     "fa_fwd",
     "fa_fwd_ex",
     "fa_fwd_fp8",
+    "fa_fwd_fp8_ex",
     "fa_bwd",
     "fa_bwd_ex",
     "fa_bwd_workspace_size",
@@ -27,6 +28,7 @@ __all__ = [
     "flash_attn_bwd",
     "flash_attn_varlen_bwd",
     "flash_attn_fwd_fp8",
+    "flash_attn_varlen_fp8",
     "flash_attn_decode",
     "flash_attn_decode_paged",
     "flash_attn_varlen",
@@ -36,7 +38,8 @@ __all__ = [
 
 def __getattr__(name):  # torch-facing wrappers are imported lazily
     if name in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_varlen_bwd", "flash_attn_fwd_fp8",
-                "flash_attn_varlen", "flash_attn_decode", "flash_attn_decode_paged",
+                "flash_attn_varlen_fp8", "flash_attn_varlen", "flash_attn_decode",
+                "flash_attn_decode_paged",
                 "decode_workspace", "FAError"):
         from . import attention
 

@@ -40,6 +40,8 @@ SIGNATURES = {
                        _I, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _I, _I, _I,
                         _I, _P]),
+    "fa_fwd_fp8_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _F,
+                           _F, _F, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -99,6 +101,14 @@ def fa_fwd_fp8(q8, k8, vt8, o, lse, B, Hq, Hkv, Lq, Lk, D, vt_stride, scale, q_d
     return load().fa_fwd_fp8(q8, k8, vt8, o, lse, B, Hq, Hkv, Lq, Lk, D, vt_stride, scale,
                              q_descale, k_descale, v_descale, causal, window_left, window_right,
                              out_dtype, stream)
+
+
+def fa_fwd_fp8_ex(q8, k8, vt8, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Lq, Lk, total_q,
+                  total_k, D, vt_stride, scale, q_descale, k_descale, v_descale, causal,
+                  window_left, window_right, out_dtype, stream) -> int:
+    return load().fa_fwd_fp8_ex(q8, k8, vt8, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Lq,
+                                Lk, total_q, total_k, D, vt_stride, scale, q_descale, k_descale,
+                                v_descale, causal, window_left, window_right, out_dtype, stream)
 
 
 def fa_decode_workspace_size(B, Hq, D, num_splits) -> int:

@@ -160,6 +160,49 @@ def flash_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch
     return dq, dk, dv
 
 
+def flash_attn_varlen_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                          max_seqlen_q: int, max_seqlen_k: int, *, q_descale: float,
+                          k_descale: float, v_descale: float, softmax_scale=None,
+                          causal: bool = False, window=(-1, -1), out_dtype=torch.bfloat16,
+                          out=None, lse=None):
+    """FP8 forward over packed sequences: q8 [total_q,Hq,D], k8 [total_k,Hkv,D]
+    e4m3; vt8 [Hkv,D,S] e4m3 (V transposed, key row r of k8 at column r, S a
+    multiple of 64 >= total_k + 64, columns past total_k zero); cu_seqlens_*
+    int32 [B+1] on the device.  Returns (o [total_q,Hq,D] in out_dtype, lse
+    [Hq,total_q])."""
+    for t, n in ((q8, "q8"), (k8, "k8"), (vt8, "vt8"), (cu_seqlens_q, "cu_seqlens_q"),
+                 (cu_seqlens_k, "cu_seqlens_k")):
+        _check_dev(t, n)
+    q8, k8, vt8 = _as_bytes(q8, "q8"), _as_bytes(k8, "k8"), _as_bytes(vt8, "vt8")
+    if q8.dim() != 3 or k8.dim() != 3 or vt8.dim() != 3:
+        raise ValueError("expected q8 [total_q,Hq,D], k8 [total_k,Hkv,D], vt8 [Hkv,D,S]")
+    total_q, Hq, D = q8.shape
+    total_k, Hkv, Dk = k8.shape
+    if Dk != D or tuple(vt8.shape[:2]) != (Hkv, D):
+        raise ValueError("shape mismatch between q8, k8 and vt8")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    if out_dtype not in _DTYPES:
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    B = cu_seqlens_q.shape[0] - 1
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty((total_q, Hq, D), dtype=out_dtype, device=q8.device) if out is None else out
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q8.device)
+    st = _abi.fa_fwd_fp8_ex(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B,
+                            Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, D,
+                            vt8.shape[2], scale, float(q_descale), float(k_descale),
+                            float(v_descale), 1 if causal else 0, int(window[0]), int(window[1]),
+                            _DTYPES[out_dtype], _stream_handle(q8.device))
+    if st != _abi.FA_OK:
+        raise FAError(st, "fa_fwd_fp8_ex")
+    return out, lse
+
+
 def flash_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                       cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
                       softmax_scale=None, causal: bool = False, window=(-1, -1), out=None,

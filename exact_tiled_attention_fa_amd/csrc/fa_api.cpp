@@ -115,15 +115,26 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   return ok();
 }
 
-fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, float* lse, int B,
-                     int Hq, int Hkv, int Lq, int Lk, int D, int vt_stride, float scale,
-                     float q_descale, float k_descale, float v_descale, int causal,
-                     int window_left, int window_right, fa_dtype out_dtype, hipStream_t stream) {
+fa_status fa_fwd_fp8_ex(const void* q8, const void* k8, const void* vt8, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                        int Lq, int Lk, int total_q, int total_k, int D, int vt_stride,
+                        float scale, float q_descale, float k_descale, float v_descale,
+                        int causal, int window_left, int window_right, fa_dtype out_dtype,
+                        hipStream_t stream) {
   FA_TRY(check_ptr(q8, "q8"));
   FA_TRY(check_ptr(k8, "k8"));
   FA_TRY(check_ptr(vt8, "vt8"));
   FA_TRY(check_ptr(o, "o"));
   FA_TRY(check_ptr(lse, "lse"));
+  const bool packed = cu_seqlens_q != nullptr || cu_seqlens_k != nullptr;
+  if (packed) {
+    if (!cu_seqlens_q || !cu_seqlens_k)
+      return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");
+    if (((uintptr_t)cu_seqlens_q & 3u) || ((uintptr_t)cu_seqlens_k & 3u))
+      return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens arrays are not 4-byte aligned");
+    if (total_q < 1 || total_k < 1)
+      return fail(FA_ERR_INVALID_ARGUMENT, "total_q=%d and total_k=%d must be >= 1", total_q, total_k);
+  }
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || D < 1)
     return fail(FA_ERR_INVALID_ARGUMENT,
                 "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d)", B, Hq, Hkv, Lq, Lk, D);
@@ -136,18 +147,24 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, f
   if (out_dtype != FA_F16 && out_dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)out_dtype);
   if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 head_dim %d not in {64, 128}", D);
-  if (vt_stride < Lk || vt_stride % 64 != 0)
-    return fail(FA_ERR_INVALID_ARGUMENT, "vt_stride=%d must be a multiple of 64 and >= Lk=%d",
-                vt_stride, Lk);
+  // Key tiles read 64 columns of V^T from a 16-aligned start: dense rows hold
+  // Lk keys (padded to 64), packed rows total_k keys plus 64 columns of
+  // padding.
+  const long long vt_need = packed ? (long long)total_k + 64 : (long long)Lk;
+  if (vt_stride % 64 != 0 || vt_stride < vt_need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "vt_stride=%d must be a multiple of 64 and >= %lld",
+                vt_stride, vt_need);
   if ((long long)D * vt_stride >= (1LL << 32))
     return fail(FA_ERR_INVALID_ARGUMENT, "D * vt_stride must be < 2^32");
   if ((long long)Hkv * D >= (1LL << 25) || (long long)Hq * D >= (1LL << 25))
     return fail(FA_ERR_INVALID_ARGUMENT, "Hq * D and Hkv * D must be < 2^25");
-  if ((long long)B * Lq * Hq > 0x7fffffffLL || (long long)B * Lk * Hkv > 0x7fffffffLL)
+  const long long rows_q = packed ? (long long)total_q : (long long)B * Lq;
+  const long long rows_k = packed ? (long long)total_k : (long long)B * Lk;
+  if (rows_q * Hq > 0x7fffffffLL || rows_k * Hkv > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
   if (((long long)Lq + 127) / 128 * B * Hq > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (Lq/128 * B * Hq > 2^31-1)");
-  const long long span = (long long)B * Lq + (long long)B * Lk;
+  const long long span = rows_q + rows_k;
   const bool windowed = window_left >= 0 || window_right >= 0;
   if (windowed && span > (1LL << 30))
     return fail(FA_ERR_INVALID_ARGUMENT, "windowed attention needs query + key rows <= 2^30");
@@ -156,9 +173,22 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, f
                 (window_left < 0 || window_left >= span) ? -1 : window_left,
                 (window_right < 0 || window_right >= span) ? -1 : window_right,
                 out_dtype == FA_BF16 ? 1 : 0};
+  a.cu_q = packed ? cu_seqlens_q : nullptr;
+  a.cu_k = packed ? cu_seqlens_k : nullptr;
+  a.total_q = packed ? total_q : 0;
+  a.total_k = packed ? total_k : 0;
   hipError_t e = fa::launch_fwd_fp8(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_fp8 launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Lq, int Lk, int D, int vt_stride, float scale,
+                     float q_descale, float k_descale, float v_descale, int causal,
+                     int window_left, int window_right, fa_dtype out_dtype, hipStream_t stream) {
+  return fa_fwd_fp8_ex(q8, k8, vt8, o, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, 0, 0, D,
+                       vt_stride, scale, q_descale, k_descale, v_descale, causal, window_left,
+                       window_right, out_dtype, stream);
 }
 
 size_t fa_decode_workspace_size(int B, int Hq, int D, int num_splits) {

@@ -30,6 +30,12 @@
 //   * K and V^T tiles stream HBM -> LDS with LDS-direct copies, two stages.
 //   * O is staged through the tile arrays and written as whole rows with
 //     non-temporal stores.
+//   * Packed sequences (cumulative offsets cu_q / cu_k, the block-diagonal
+//     structured mask of "5 years, 10K stars: xformers", cloud.tencent.com):
+//     V^T is [Hkv, D, stride] with key row r of the packed K at column r, and
+//     a sequence's key tiles start at its first key rounded down to 16, so
+//     that the 16-byte copies stay aligned; the few keys before its first
+//     (the previous sequence's) count as invisible.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -50,7 +56,10 @@ struct Fp8Params {
   const uint8_t* VT;
   uint16_t* O;
   float* LSE;
-  int B, Hq, Hkv, Lq, Lk, vt_stride;
+  const int* cu_q;  // nullptr: dense batch
+  const int* cu_k;
+  int total_q, total_k;
+  int B, Hq, Hkv, Lq, Lk, vt_stride;  // packed: Lq, Lk are the longest lengths
   int win_left, win_right;
   float scale2;  // |scale * q_descale * k_descale| * log2(e)
   float thr;     // lazy-rescale slack in raw score units
@@ -91,36 +100,60 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   __shared__ __attribute__((aligned(16))) uint8_t sK1[KT];
   __shared__ __attribute__((aligned(16))) uint8_t sV1[VTB];
 
-  const int B = prm.B, Hq = prm.Hq, Hkv = prm.Hkv, Lq = prm.Lq, Lk = prm.Lk;
+  const int B = prm.B, Hq = prm.Hq, Hkv = prm.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
 
-  const int nqt = (Lq + kPBM - 1) / kPBM;
+  const int nqt = (prm.Lq + kPBM - 1) / kPBM;
   int b, h, qt;
   xcd_work_item(B, Hq, nqt, prm.xcd_w, b, h, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int kvh = h / (Hq / Hkv);
-  const int shift = Lk - Lq;
+  // This sequence's rows.  Packed offsets are clamped into the tensors so
+  // that inconsistent offsets cannot move an access out of bounds.
+  int qs, Lq, ks, Lk;
+  if (prm.cu_q) {
+    qs = min(max(prm.cu_q[b], 0), prm.total_q);
+    Lq = min(max(prm.cu_q[b + 1], qs), prm.total_q) - qs;
+    ks = min(max(prm.cu_k[b], 0), prm.total_k);
+    Lk = min(max(prm.cu_k[b + 1], ks), prm.total_k) - ks;
+  } else {
+    qs = b * prm.Lq, Lq = prm.Lq, ks = 0, Lk = prm.Lk;
+  }
   const int q0 = qt * kPBM, qw0 = q0 + kPR * w, qrow = qw0 + l32;
+  if (q0 >= Lq) return;  // past this sequence's rows (whole workgroup)
+  const int shift = Lk - Lq;
+  // Key tiles start at a 16-key aligned column of V^T: a packed sequence
+  // whose first key is column ks walks tiles from c0 = ks rounded down to 16,
+  // and its keys are counted dlt = ks - c0 further on in tile coordinates
+  // (its own keys are dlt .. dlt+Lk-1; the dlt keys before them belong to the
+  // previous sequence and are never visible).  Dense batches have dlt = 0.
+  const int c0 = prm.cu_q ? (ks & ~15) : 0;
+  const int dlt = ks - c0;
+  const int LkA = Lk + dlt;  // end of this sequence's keys in tile coordinates
   const int wl = prm.win_left, wr = prm.win_right;
-  auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
+  auto kmin = [&](int i) { return dlt + (wl < 0 ? 0 : max(0, i + shift - wl)); };
   auto kmax = [&](int i) {
     int hi = Lk - 1;
     if (CAUSAL) hi = min(hi, i + shift);
     if (wr >= 0) hi = min(hi, i + shift + wr);
-    return hi;
+    return dlt + hi;
   };
 
   const long qstride = (long)Hq * D;
   const int kstride = Hkv * D;
-  const uint8_t* Kb = prm.K + (long)b * Lk * kstride + (long)kvh * D;
-  const uint8_t* Vb = prm.VT + ((long)b * Hkv + kvh) * D * (long)prm.vt_stride;
+  // dense: K [B, Lk, Hkv, D], V^T [B, Hkv, D, vt_stride]; packed: K [total_k,
+  // Hkv, D], V^T [Hkv, D, vt_stride] with key row r of K at column r
+  const uint8_t* Kb = prm.cu_q ? prm.K + (long)c0 * kstride + (long)kvh * D
+                               : prm.K + (long)b * Lk * kstride + (long)kvh * D;
+  const uint8_t* Vb = prm.cu_q ? prm.VT + (long)kvh * D * (long)prm.vt_stride + c0
+                               : prm.VT + ((long)b * Hkv + kvh) * D * (long)prm.vt_stride;
 
   // Q^T operand: lane holds query qrow, dims 64m + 32hf .. +31 for MFMA m.
   i32x8 qf[D / 64];
   {
-    const uint8_t* qr = prm.Q + ((long)b * Lq + min(qrow, Lq - 1)) * qstride + (long)h * D;
+    const uint8_t* qr = prm.Q + ((long)qs + min(qrow, Lq - 1)) * qstride + (long)h * D;
 #pragma unroll
     for (int m = 0; m < D / 64; ++m) {
       const u32x4 x0 = *reinterpret_cast<const u32x4*>(qr + 64 * m + 32 * hf) ^ prm.qxor;
@@ -161,14 +194,15 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   const uint8_t* kbase = Kb + (long)t_first * ktile;
   auto issue = [&](int t, uint8_t* dK, uint8_t* dV) {
     const int j0 = t * kPBN;
-    const bool whole = j0 + kPBN <= Lk;
+    const bool whole = j0 + kPBN <= LkA;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       uint32_t o = koff[i];
-      if (!whole) o -= (uint32_t)(((j0 + krow[i]) - min(j0 + krow[i], Lk - 1)) * kstride);
+      if (!whole) o -= (uint32_t)(((j0 + krow[i]) - min(j0 + krow[i], LkA - 1)) * kstride);
       load_lds16_off(kbase, o, dK + (i * kPW + wu) * 1024);
     }
-    // V^T columns j0 .. j0+63 lie inside the row (stride a multiple of 64 >= Lk)
+    // V^T columns j0 .. j0+63 lie inside the row: dense, the stride is a
+    // multiple of 64 >= Lk; packed, it is >= total_k + 64 and j0 <= dlt + Lk - 1
 #pragma unroll
     for (int i = 0; i < NV; ++i) load_lds16_off(Vb + j0, voff[i], dV + (i * kPW + wu) * 1024);
     kbase += ktile;
@@ -297,12 +331,12 @@ void fwd_fp8_kernel(const Fp8Params prm) {
     if (q < Lq)
       __builtin_nontemporal_store(
           *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))),
-          reinterpret_cast<u32x4*>(prm.O + ((long)b * Lq + q) * qstride + (long)h * D + 8 * c));
+          reinterpret_cast<u32x4*>(prm.O + ((long)qs + q) * qstride + (long)h * D + 8 * c));
   }
-  if (hf == 0 && qrow < Lq)
+  if (hf == 0 && qrow < Lq)  // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
     __builtin_nontemporal_store(
         l > 0.f ? (m_ref * scale2 + __builtin_log2f(l) - 8.f) * kLn2 : -INFINITY,
-        prm.LSE + ((long)b * Hq + h) * Lq + qrow);
+        prm.LSE + (prm.cu_q ? (long)h * prm.total_q + qs + qrow : ((long)b * Hq + h) * Lq + qrow));
 }
 
 template <int D, typename OT>
@@ -313,6 +347,10 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
   p.VT = (const uint8_t*)a.vt;
   p.O = (uint16_t*)a.o;
   p.LSE = a.lse;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
   p.B = a.B;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;

@@ -89,16 +89,19 @@ struct BwdArgs {
 };
 
 struct Fp8Args {
-  const void* q;   // e4m3 [B, Lq, Hq, D]
-  const void* k;   // e4m3 [B, Lk, Hkv, D]
-  const void* vt;  // e4m3 [B, Hkv, D, vt_stride]
-  void* o;         // [B, Lq, Hq, D] bf16 / fp16
-  float* lse;      // [B, Hq, Lq]
+  const void* q;   // e4m3 [B, Lq, Hq, D]; packed [total_q, Hq, D]
+  const void* k;   // e4m3 [B, Lk, Hkv, D]; packed [total_k, Hkv, D]
+  const void* vt;  // e4m3 [B, Hkv, D, vt_stride]; packed [Hkv, D, vt_stride]
+  void* o;         // [B, Lq, Hq, D] bf16 / fp16; packed [total_q, Hq, D]
+  float* lse;      // [B, Hq, Lq]; packed [Hq, total_q]
   int B, Hq, Hkv, Lq, Lk, D, vt_stride;
   float scale, q_descale, k_descale, v_descale;
   int causal;
   int win_left, win_right;
   int out_bf16;
+  const int* cu_q = nullptr;  // packed sequences: offsets [B + 1], else nullptr
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

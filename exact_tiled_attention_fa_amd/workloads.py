@@ -227,6 +227,22 @@ def fp8_inputs(B, Lq, Lk, Hq, Hkv, D, seed, *, q_scale=1.0):
     return cast(q), cast(k), vt, 1.0 / FP8_MULT
 
 
+def fp8_varlen_inputs(total_q, total_k, Hq, Hkv, D, seed, *, q_scale=1.0):
+    """Packed e4m3 codes as uint8: q8 [total_q,Hq,D], k8 [total_k,Hkv,D] and
+    vt8 [Hkv,D,S] (V transposed, key row r at column r, S = total_k + 64
+    rounded up to 64, zero columns past total_k), plus the descale 1/16 of
+    each.  Draw order and casts as fp8_inputs."""
+    g = _gen(seed)
+    q = torch.randn((total_q, Hq, D), generator=g, dtype=torch.float32) * q_scale
+    k = torch.randn((total_k, Hkv, D), generator=g, dtype=torch.float32)
+    v = torch.randn((total_k, Hkv, D), generator=g, dtype=torch.float32)
+    cast = lambda x: (x * FP8_MULT).to(torch.float8_e4m3fn).view(torch.uint8)
+    S = (total_k + 64 + 63) // 64 * 64
+    vt = torch.zeros((Hkv, D, S), dtype=torch.uint8)
+    vt[..., :total_k] = cast(v).permute(1, 2, 0)
+    return cast(q), cast(k), vt, 1.0 / FP8_MULT
+
+
 def decode_lengths(cfg: Decode) -> torch.Tensor:
     """Per-sequence cache lengths, uniform on [len_lo, len_hi], int32 [B]."""
     g = _gen(cfg.seed)

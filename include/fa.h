@@ -142,6 +142,34 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, f
                      int window_left, int window_right, fa_dtype out_dtype, hipStream_t stream);
 
 /*
+ * fa_fwd_fp8_ex -- fa_fwd_fp8 also for sequences packed back to back, the
+ * block-diagonal structured mask of "5 years, 10K stars: xformers"
+ * (cloud.tencent.com), as fa_fwd_ex has it for 16-bit inputs.
+ *
+ *   cu_seqlens_q, cu_seqlens_k   NULL (dense: exactly fa_fwd_fp8) or device
+ *               int32 [B + 1] offsets, as in fa_fwd_ex: sequence b is query
+ *               rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows
+ *               cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 and attends only to
+ *               itself.  Offsets are clamped into [0, total] on the device.
+ *   packed:  q8 [total_q, Hq, D], k8 [total_k, Hkv, D], o [total_q, Hq, D],
+ *            lse float32 [Hq, total_q];
+ *            vt8 [Hkv, D, vt_stride]: V transposed, key row r of k8 at column r;
+ *            vt_stride a multiple of 64 and >= total_k + 64.  Columns
+ *            total_k .. vt_stride-1 are read (each sequence's key tiles start
+ *            at its first key rounded down to 16) and must hold finite codes.
+ *   Lq, Lk      dense: the lengths; packed: the longest query / key sequence
+ *               (the grid is sized by Lq).
+ *   total_q, total_k   packed: the row counts of q8 / k8 (ignored when dense).
+ *   other arguments as in fa_fwd_fp8.
+ */
+fa_status fa_fwd_fp8_ex(const void* q8, const void* k8, const void* vt8, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                        int Lq, int Lk, int total_q, int total_k, int D, int vt_stride,
+                        float scale, float q_descale, float k_descale, float v_descale,
+                        int causal, int window_left, int window_right, fa_dtype out_dtype,
+                        hipStream_t stream);
+
+/*
  * fa_decode_workspace_size -- bytes of device workspace fa_decode needs for
  * these sizes: float32 partial outputs [B, Hq, num_splits, D] followed by
  * float32 partial logsumexps [B, Hq, num_splits].  Returns 0 for invalid sizes.

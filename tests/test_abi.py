@@ -36,7 +36,8 @@ def lib():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size",
+        ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_fp8_ex", "fa_bwd", "fa_bwd_ex",
+         "fa_bwd_workspace_size",
          "fa_decode",
          "fa_decode_paged", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
 
@@ -276,6 +277,42 @@ def fp8(**kw):
 def test_fp8_rejects(lib, kw, status, text):
     assert fp8(**kw) == status
     assert text in _abi.fa_last_error()
+
+
+def fp8_ex(**kw):
+    a = dict(q=A16, k=A16, vt=A16, o=A16, lse=A16, cu_q=None, cu_k=None, B=1, Hq=2, Hkv=1, Lq=8,
+             Lk=8, total_q=0, total_k=0, D=128, vts=64, scale=0.1, qd=0.0625, kd=0.0625,
+             vd=0.0625, causal=1, wl=-1, wr=-1, dtype=_abi.FA_BF16, stream=None)
+    a.update(kw)
+    return _abi.fa_fwd_fp8_ex(*a.values())
+
+
+PACKED8 = dict(cu_q=A16, cu_k=A16, B=2, Lq=8, Lk=8, total_q=16, total_k=16, vts=128)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(cu_q=A16), _abi.FA_ERR_INVALID_ARGUMENT, "both be set"),
+    (dict(cu_k=A16), _abi.FA_ERR_INVALID_ARGUMENT, "both be set"),
+    (dict(PACKED8, cu_q=A16 + 2), _abi.FA_ERR_INVALID_ARGUMENT, "4-byte aligned"),
+    (dict(PACKED8, total_q=0), _abi.FA_ERR_INVALID_ARGUMENT, "total_q=0"),
+    (dict(PACKED8, vts=64), _abi.FA_ERR_INVALID_ARGUMENT, "vt_stride=64"),
+    (dict(PACKED8, vts=100), _abi.FA_ERR_INVALID_ARGUMENT, "multiple of 64"),
+    (dict(PACKED8, D=256), _abi.FA_ERR_UNSUPPORTED, "fp8 head_dim 256"),
+    (dict(PACKED8, total_q=1 << 30, Hq=4, Hkv=1), _abi.FA_ERR_INVALID_ARGUMENT, "2^31-1"),
+])
+def test_fp8_ex_rejects(lib, kw, status, text):
+    assert fp8_ex(**kw) == status
+    assert text in _abi.fa_last_error()
+
+
+def test_fp8_is_fp8_ex_without_offsets(lib):
+    """fa_fwd_fp8 validates exactly as fa_fwd_fp8_ex with NULL offsets."""
+    for kw in (dict(vt=None), dict(vts=32), dict(vts=64, Lk=65), dict(qd=0.0), dict(D=256),
+               dict(dtype=5), dict(Hq=3, Hkv=2)):
+        st1 = fp8(**kw)
+        e1 = _abi.fa_last_error()
+        st2 = fp8_ex(**kw)
+        assert (st1, e1) == (st2, _abi.fa_last_error())
 
 
 def test_last_error_is_per_thread(lib):

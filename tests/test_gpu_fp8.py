@@ -116,3 +116,74 @@ def test_fp8_deterministic(gpu):
     a = run_fp8(q8, k8, vt8, ds, 0.088, True, (-1, -1), torch.bfloat16, gpu)
     b = run_fp8(q8, k8, vt8, ds, 0.088, True, (-1, -1), torch.bfloat16, gpu)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# Packed sequences (fa_fwd_fp8_ex): query / key length mixes with an empty
+# query sequence, an empty key sequence, starts off the 16-key grid and on it,
+# and Lk != Lq within one batch.
+VARLEN_MIXES = [
+    ([5, 0, 37, 64, 1, 130], [5, 20, 37, 64, 1, 130]),
+    ([40, 17, 200], [40, 17, 200]),
+    ([16, 48, 64], [16, 48, 64]),
+    ([33, 1, 90], [70, 129, 0]),
+]
+
+
+def check_varlen(lens_q, lens_k, Hq, Hkv, D, causal, seed, gpu, *, window=(-1, -1), scale=None,
+                 out_dtype=torch.bfloat16):
+    from exact_tiled_attention_fa_amd.attention import flash_attn_varlen_fp8
+
+    scale = f32(scale if scale is not None else D ** -0.5)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    total_q, total_k = int(cu_q[-1]), int(cu_k[-1])
+    q8, k8, vt8, ds = W.fp8_varlen_inputs(total_q, total_k, Hq, Hkv, D, seed)
+    tag = (f"fp8 varlen q={lens_q} k={lens_k} Hq={Hq} Hkv={Hkv} D={D} causal={causal} "
+           f"window={window}")
+    say(tag)
+    o, lse = flash_attn_varlen_fp8(q8.to(gpu), k8.to(gpu), vt8.to(gpu),
+                                   torch.from_numpy(cu_q).to(gpu), torch.from_numpy(cu_k).to(gpu),
+                                   max(lens_q), max(lens_k), q_descale=ds, k_descale=ds,
+                                   v_descale=ds, softmax_scale=scale, causal=causal, window=window,
+                                   out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    q = oracle.e4m3_decode(q8) * ds
+    k = oracle.e4m3_decode(k8) * ds
+    v = np.ascontiguousarray(oracle.e4m3_decode(vt8)[..., :total_k].transpose(2, 0, 1)) * ds
+    o_ref, l_ref = oracle.varlen_ref(q, k, v, cu_q, cu_k, scale, causal, window=window)
+    mag, _ = oracle.varlen_ref(q, k, np.abs(v), cu_q, cu_k, scale, causal, window=window)
+    compare_fp8(o.cpu(), lse.cpu(), o_ref, l_ref, mag, out_dtype, tag)
+
+
+@pytest.mark.parametrize("window", [(-1, -1), (32, 8)], ids=["nowin", "win"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mix", range(len(VARLEN_MIXES)))
+def test_fp8_varlen(mix, D, causal, window, gpu):
+    lq, lk = VARLEN_MIXES[mix]
+    check_varlen(lq, lk, 4, 2, D, causal, 300 + 10 * mix + D, gpu, window=window)
+
+
+@pytest.mark.parametrize("g", [1, 4])
+def test_fp8_varlen_gqa_f16_out(g, gpu):
+    check_varlen([77, 3, 150], [77, 3, 150], 8, 8 // g, 128, True, 340 + g, gpu,
+                 out_dtype=torch.float16, scale=-0.09)
+
+
+def test_fp8_varlen_equals_dense_batch(gpu):
+    """Equal-length sequences starting on the 64-key grid take the same tile
+    walk as the dense batch: bit-identical O and lse."""
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd_fp8, flash_attn_varlen_fp8
+
+    B, L, Hq, Hkv, D = 3, 192, 4, 2, 128
+    q8, k8, vt8, ds = W.fp8_varlen_inputs(B * L, B * L, Hq, Hkv, D, 350)
+    cu = torch.arange(0, B * L + 1, L, dtype=torch.int32)
+    kw = dict(q_descale=ds, k_descale=ds, v_descale=ds, causal=True)
+    o_p, l_p = flash_attn_varlen_fp8(q8.to(gpu), k8.to(gpu), vt8.to(gpu), cu.to(gpu), cu.to(gpu),
+                                     L, L, **kw)
+    vt_dense = vt8[..., :B * L].reshape(Hkv, D, B, L).permute(2, 0, 1, 3).contiguous()
+    o_d, l_d = flash_attn_fwd_fp8(q8.view(B, L, Hq, D).to(gpu), k8.view(B, L, Hkv, D).to(gpu),
+                                  vt_dense.to(gpu), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p.cpu().view(B, L, Hq, D), o_d.cpu())
+    assert torch.equal(l_p.cpu().view(Hq, B, L).permute(1, 0, 2), l_d.cpu())

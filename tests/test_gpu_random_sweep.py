@@ -190,3 +190,22 @@ def test_random_decode(case, gpu):
     o, lse = decode_run(q, kc, vc, lens_t, scale, splits, gpu)
     o_ref, l_ref = oracle.decode_ref(q, kc, vc, lens, scale)
     compare(o, lse, o_ref, l_ref, tag)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_forward_fp8_packed(case, gpu):
+    """The FP8 forward over random packed mixes (empty sequences, starts off
+    the 16-key grid), head groups, D, causal, windows and output types."""
+    from test_gpu_fp8 import check_varlen
+
+    rng = np.random.default_rng(9000 + case)
+    B = int(rng.integers(1, 6))
+    lens_q = draw_lens(rng, B, 300)
+    lens_k = lens_q if rng.random() < 0.5 else draw_lens(rng, B, 300)
+    Hq, Hkv = draw_heads(rng)
+    D = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    window = draw_window(rng)
+    out_dtype = DTYPES[int(rng.integers(0, 2))]
+    check_varlen(lens_q, lens_k, Hq, Hkv, D, causal, 9500 + case, gpu, window=window,
+                 out_dtype=out_dtype)
