@@ -164,3 +164,37 @@ def test_paged_full_size_sampled(fmt, gpu):
     o_ref, l_ref = oracle.decode_paged_ref(q, kp, vp, table, lens, scale, k_scales=ks,
                                            v_scales=vs, heads=heads)
     compare(o, lse, o_ref, l_ref, f"paged full-size {fmt} seqs={seqs}")
+
+
+@pytest.mark.parametrize("fmt", ["native", "kv8"])
+def test_decode_paged_large_pool(fmt, gpu):
+    """A pool of 8400 pages x 256 slots x 8 K/V heads x 128 (2.2e9 elements)
+    with every page the sequences own at its top, past element 2^31; the rest
+    of the pool is NaN (int8: NaN scales)."""
+    k8, v8 = FORMATS[fmt]
+    B, Hq, Hkv, D, ps = 3, 32, 8, 128, 256
+    lens = [3000, 77, 2049]
+    q, kp, vp, ks, vs, table, lens_t = make_paged(B, Hq, Hkv, D, lens, ps, torch.bfloat16, 370,
+                                                  k_int8=k8, v_int8=v8, extra_pages=1)
+    big = 8400
+    off = big - kp.shape[0]
+
+    def grow(x, fill):
+        if x is None:
+            return None
+        y = torch.full((big,) + tuple(x.shape[1:]), fill, dtype=x.dtype)
+        y[off:] = x
+        return y
+
+    kp = grow(kp, 127 if k8 else float("nan"))
+    vp = grow(vp, 127 if v8 else float("nan"))
+    ks, vs = grow(ks, float("nan")), grow(vs, float("nan"))
+    table = table + off
+    assert kp.numel() > 2 ** 31 and int(table.min()) * ps * Hkv * D > 2 ** 31
+    scale = f32(D ** -0.5)
+    say(f"paged large pool {fmt} lens={lens}")
+    o, lse = run(q, kp, vp, ks, vs, table, lens_t, scale, 8, gpu)
+    heads = [(b, h) for b in range(B) for h in (0, 13, 31)]
+    o_ref, l_ref = oracle.decode_paged_ref(q, kp, vp, table, lens_t, scale, k_scales=ks,
+                                           v_scales=vs, heads=heads)
+    compare(o, lse, o_ref, l_ref, f"large pool {fmt}")

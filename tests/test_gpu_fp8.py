@@ -187,3 +187,34 @@ def test_fp8_varlen_equals_dense_batch(gpu):
     torch.cuda.synchronize()
     assert torch.equal(o_p.cpu().view(B, L, Hq, D), o_d.cpu())
     assert torch.equal(l_p.cpu().view(Hq, B, L).permute(1, 0, 2), l_d.cpu())
+
+
+def test_fp8_long_sequence_sampled_rows(gpu):
+    """Q and O of 147456 rows x 128 heads x 128 dims (2.4e9 elements, offsets
+    past 2^31; Q repeats one random 16-head block over the 8 head groups).
+    A causal row i with Lq = Lk is one query against its i + 1 first keys:
+    the oracle's decode_ref on the decoded values gives it (and, on |v|, the
+    magnitude the bound needs)."""
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd_fp8
+
+    B, L, Hq, Hkv, D = 1, 147456, 128, 8, 128
+    q16, k8, vt8, ds = W.fp8_inputs(B, L, L, 16, Hkv, D, 360)
+    q8 = q16.repeat(1, 1, Hq // 16, 1)
+    assert q8.numel() > 2 ** 31
+    scale = f32(D ** -0.5)
+    say(f"fp8 long causal L={L} Hq={Hq} Hkv={Hkv} D={D}")
+    o, lse = flash_attn_fwd_fp8(q8.to(gpu), k8.to(gpu), vt8.to(gpu), q_descale=ds, k_descale=ds,
+                                v_descale=ds, softmax_scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    k = oracle.e4m3_decode(k8) * ds
+    v = np.ascontiguousarray(oracle.e4m3_decode(vt8)[..., :L].transpose(0, 3, 1, 2)) * ds
+    heads = [0, 17, 120, 127]
+    sel = np.array(heads)
+    hs = [(0, h) for h in heads]
+    for i in [0, 1, 63, 64, 127, 128, 65537, L - 1]:
+        qi = oracle.e4m3_decode(q8[:, i]) * ds
+        o_ref, l_ref = oracle.decode_ref(qi, k, v, [i + 1], scale, heads=hs)
+        mag, _ = oracle.decode_ref(qi, k, np.abs(v), [i + 1], scale, heads=hs)
+        compare_fp8(o[:, i][:, sel], lse[:, sel, i], o_ref[:, sel], l_ref[:, sel], mag[:, sel],
+                    torch.bfloat16, f"row {i}")
