@@ -173,6 +173,36 @@ def test_bwd_ignores_workspace_contents(packed, gpu):
         assert torch.equal(a, b)
 
 
+def test_bwd_offsets_past_2_31(gpu):
+    """136 batches made of 17 copies of 8 random ones (L = 512, 128 heads,
+    D = 256: 2.3e9 elements per tensor, so element offsets run past 2^31).
+    With no atomics every block's arithmetic is fixed, so the last copy's
+    gradients, at the far end of memory, are bit-identical to the first
+    copy's; the first copy matches the oracle on two (batch, head) slices."""
+    from exact_tiled_attention_fa_amd.attention import flash_attn_bwd, flash_attn_fwd
+
+    Bs, R, L, H, D = 8, 17, 512, 128, 256
+    q, k, v = W.randn_qkv(Bs, L, L, H, H, D, torch.bfloat16, 380)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(381)).to(torch.bfloat16)
+    Q, K, V, DO = (t.repeat(R, 1, 1, 1).to(gpu) for t in (q, k, v, do))
+    assert Q.numel() > 2 ** 31
+    scale = f32(D ** -0.5)
+    say(f"bwd past 2^31: B={Bs * R} L={L} H={H} D={D}")
+    o, lse = flash_attn_fwd(Q, K, V, softmax_scale=scale, causal=False)
+    dq, dk, dv = flash_attn_bwd(Q, K, V, o, lse, DO, softmax_scale=scale, causal=False)
+    torch.cuda.synchronize()
+    first = [t[:Bs].cpu() for t in (dq, dk, dv)]
+    last = [t[-Bs:].cpu() for t in (dq, dk, dv)]
+    del Q, K, V, DO, o, lse, dq, dk, dv
+    for a, b in zip(first, last):
+        assert torch.equal(a, b)
+    heads = [(0, 0), (Bs - 1, H - 1)]
+    r = oracle.attention_bwd_ref(q, k, v, do, scale, False, bounds=True, kv_heads=heads)
+    compare_grad(first[0], r[0], r[3], torch.bfloat16, f"dq {heads}")
+    compare_grad(first[1], r[1], r[4], torch.bfloat16, f"dk {heads}")
+    compare_grad(first[2], r[2], r[5], torch.bfloat16, f"dv {heads}")
+
+
 def test_bwd_full_size_sampled(gpu):
     """The Llama-2-7B-shaped causal workload (B=4, H=32, L=4096, D=128, bf16)
     in the launch the benchmark times; the oracle computes two whole K/V
