@@ -494,7 +494,7 @@ def main():
         print(json.dumps(t))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path "
+        sys.exit("bench.py measures one GPU only: the library has no multi-GPU path "
                  "(run with --gpus 1).")
     import numpy as np
     import torch
