@@ -265,6 +265,46 @@ def test_varlen_equals_dense_batch(gpu):
         assert torch.equal(l1.permute(1, 0, 2).reshape(H, B * L), l2)
 
 
+def test_varlen_offsets_past_2_31(gpu):
+    """Packed causal prefill with 128 query and 128 K/V heads of 128 dims over
+    lengths [131072, 16400]: the second sequence starts at element 2^31 of
+    Q, K, V and O.  Each head gathers one of 16 drawn heads for Q, K and V
+    through three different maps, so the (Q, K, V) triple differs between
+    the checked heads.  Query row i of a sequence sees that sequence's keys
+    0..i, which is one query against a cache of length i + 1 (decode_ref)."""
+    from exact_tiled_attention_fa_amd.attention import flash_attn_varlen
+
+    lens, H, D = [131072, 16400], 128, 128
+    T = sum(lens)
+    assert lens[0] * H * D == 2 ** 31
+    gen = torch.Generator().manual_seed(96)
+    blocks = [torch.randn((T, 16, D), generator=gen).to(torch.bfloat16).to(gpu) for _ in range(3)]
+    h = torch.arange(H)
+    maps = [h % 16, (5 * h + h // 16) % 16, (3 * h + 7 * (h // 16)) % 16]
+    q, k, v = (b.index_select(1, m.to(gpu)) for b, m in zip(blocks, maps))
+    del blocks
+    assert q.numel() > 2 ** 31 and k.numel() > 2 ** 31
+    cu = torch.tensor([0, lens[0], T], dtype=torch.int32, device=gpu)
+    scale = f32(D ** -0.5)
+    say(f"packed causal prefill lens={lens} H={H} D={D}")
+    o, lse = flash_attn_varlen(q, k, v, cu, cu, max(lens), max(lens), softmax_scale=scale,
+                               causal=True)
+    torch.cuda.synchronize()
+    heads = [0, 17, 64, 127]
+    sel = torch.tensor(heads, device=gpu)
+    for s, rows in ((0, [0, 1, 127, 128, 65537, lens[0] - 1]),
+                    (1, [0, 1, 31, 32, 8191, lens[1] - 1])):
+        start = [0, lens[0]][s]
+        for i in rows:
+            r = start + i
+            kk = k[start:r + 1].index_select(1, sel).cpu()[None]
+            vv = v[start:r + 1].index_select(1, sel).cpu()[None]
+            o_ref, l_ref = oracle.decode_ref(q[r].index_select(0, sel).cpu()[None], kk, vv,
+                                             [i + 1], scale)
+            compare(o[r].index_select(0, sel).cpu()[None], lse[:, r].index_select(0, sel).cpu()[None],
+                    o_ref, l_ref, f"sequence {s} row {i}")
+
+
 @pytest.mark.parametrize("name,nheads", [("swa16k", 2), ("varlen16", 6)])
 def test_masked_full_size_sampled(name, nheads, gpu):
     """The structured-mask workloads at full size, in the launch the benchmark
