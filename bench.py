@@ -60,6 +60,8 @@ def parse():
                         "decode or the backward workloads (one JSON line)")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward workload")
     p.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward workload")
+    p.add_argument("--no-probe", action="store_true",
+                   help="skip the matrix-core ceiling probe on the prefill's operands")
     p.add_argument("--paged-format", choices=["native", "k8", "kv8"], default=None,
                    help="time only this paged-cache format")
     p.add_argument("--no-paged", action="store_true",
@@ -428,6 +430,38 @@ def time_fp8(dev, reps=10):
             "kernel": "fwd_fp8_kernel<128, bf16_t, true>"}
 
 
+def time_mfma_probe(q, dev, reps=10, iters=2048):
+    """The matrix cores' ceiling on the prefill's own data: the library's MFMA
+    probe (bf16 32x32x16 MFMAs only, in the forward step's chain pattern, two
+    waves per SIMD on every CU) timed with HIP events on the launch stream,
+    once with its operands taken from the prefill's Q and once with every
+    operand 1.0.  The MFMA rate depends on the operand values, so the first
+    figure, not the published peak, is what the forward's MFMA work can reach
+    on this data."""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd.attention import mfma_probe
+
+    ones = torch.ones(1 << 24, dtype=torch.bfloat16, device=dev)
+    res = {"about": "MFMA-only probe, bf16 32x32x16, 2 waves/SIMD, every CU; operands read "
+                    "once from the given buffer"}
+    for name, ops in (("prefill_q", q), ("constant_1", ones)):
+        out, flops = mfma_probe(ops, iters)
+        settle(lambda: mfma_probe(ops, iters, out))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            mfma_probe(ops, iters, out)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        res[name] = {"TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4)}
+    return res
+
+
 def time_masked(cfg, dev, reps=10):
     """Mean launch time (ms, HIP events on the launch stream) of one
     structured-mask workload, and its algorithmic TFLOP/s."""
@@ -642,6 +676,11 @@ def main():
     if do_pf and not args.no_masks:
         print("# structured-mask workloads", file=sys.stderr, flush=True)
         out["masks"] = {name: time_masked(cfg, dev) for name, cfg in masks.items()}
+    if do_pf and not args.no_probe:
+        print("# matrix-core ceiling probe", file=sys.stderr, flush=True)
+        out["mfma_probe"] = time_mfma_probe(q, dev)
+        out["mfma_probe"]["prefill_frac_of_prefill_q_ceiling"] = round(
+            out["value"] / out["mfma_probe"]["prefill_q"]["TFLOP/s"], 4)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         if do_pf:

@@ -25,7 +25,8 @@ OUT_DIR = PKG / "_lib"
 LIB = OUT_DIR / "libfa.so"
 OBJ_DIR = ROOT / "_build"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip",
+           "fa_probe.hip"]
 ARCH = "gfx950"
 
 

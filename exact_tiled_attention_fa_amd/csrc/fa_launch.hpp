@@ -112,6 +112,14 @@ int bwd_padded_rows(int Lq);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 
+// Matrix-core ceiling probe (a measurement helper): nblocks workgroups of
+// mfma_probe_threads(1) threads over n16 16-byte operands; out holds one float
+// per thread.
+hipError_t launch_mfma_probe(const void* ops, long n16, float* out, int nblocks, int iters,
+                             hipStream_t stream);
+double mfma_probe_flops(int nblocks, int iters);
+int mfma_probe_threads(int nblocks);
+
 // Prefill tiling, reported by fa_info().
 #ifndef FA_FWD_WAVES
 #define FA_FWD_WAVES 4

@@ -312,6 +312,29 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     int window_right, void* workspace, size_t workspace_bytes, fa_dtype dtype,
                     hipStream_t stream);
 
+/* ---- Measurement helper (not an attention operation) ----------------------
+ * The matrix cores' sustained rate on given data.  On the MI355X the MFMA rate
+ * depends on the operand values (toggling mantissas draw power and lower the
+ * clock), so the published dense peak is not reached on random inputs; timing
+ * this kernel on a workload's own operands gives the ceiling for that data.
+ * It runs v_mfma_f32_32x32x16_bf16 only, in the forward step's pattern (one
+ * 8-deep dependent chain and four 2-deep ones per iteration), two workgroups
+ * of 256 threads per compute unit.
+ *
+ * fa_probe_mfma_out_len: floats the probe writes on the current device (one
+ *   per thread); 0 if the device cannot be queried.
+ * fa_probe_mfma_bf16: operands is a device buffer of operand_bytes (a positive
+ *   multiple of 16, 16-byte aligned) read as bf16; thread t takes its 18
+ *   16-byte operands from index t*18 onward, modulo the buffer.  out (device,
+ *   out_len >= fa_probe_mfma_out_len() floats) receives each thread's
+ *   accumulator sum: exactly 4096 * iters when every operand is bf16 1.0.
+ *   iters in [1, 2^20].  *flops_per_launch (host) receives the flops one
+ *   launch executes.  Asynchronous on `stream`; owns nothing. */
+size_t fa_probe_mfma_out_len(void);
+fa_status fa_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* out,
+                             size_t out_len, int iters, double* flops_per_launch,
+                             hipStream_t stream);
+
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

@@ -39,7 +39,8 @@ def test_header_declares_the_abi():
         ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_fp8_ex", "fa_bwd", "fa_bwd_ex",
          "fa_bwd_workspace_size",
          "fa_decode",
-         "fa_decode_paged", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
+         "fa_decode_paged", "fa_decode_workspace_size", "fa_last_error", "fa_info",
+         "fa_probe_mfma_out_len", "fa_probe_mfma_bf16"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -336,3 +337,19 @@ def test_last_error_is_per_thread(lib):
     b = threading.Thread(target=worker, args=("b", dict(Hq=3, Hkv=2), "not a multiple"))
     a.start(); b.start(); a.join(); b.join()
     assert results == {"a": "ok", "b": "ok"}, results
+
+
+def test_probe_rejects(lib):
+    """The MFMA probe checks its host arguments before it asks for the device."""
+    import ctypes
+
+    fl = ctypes.c_double(0.0)
+    bad = [dict(operands=None), dict(out=None), dict(operand_bytes=0), dict(operand_bytes=24),
+           dict(iters=0), dict(iters=(1 << 20) + 1), dict(operands=A16 + 8)]
+    for kw in bad:
+        a = dict(operands=A16, operand_bytes=1 << 20, out=A16, out_len=1 << 20, iters=4)
+        a.update(kw)
+        st = _abi.fa_probe_mfma_bf16(a["operands"], a["operand_bytes"], a["out"], a["out_len"],
+                                     a["iters"], fl, None)
+        assert st == _abi.FA_ERR_INVALID_ARGUMENT, (kw, _abi.fa_last_error())
+    assert fl.value == 0.0
