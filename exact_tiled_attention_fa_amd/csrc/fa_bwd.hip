@@ -148,37 +148,6 @@ void bwd_prep_kernel(const BwdParams p) {
   }
 }
 
-// Block -> (sequence b, head h, tile rank).  Blocks start in index order,
-// so tile-major order (rank 0 of every head, then rank 1, ...) puts the
-// heaviest tiles first and the lightest in the tail.  Block i runs on XCD
-// i % 8.  When H is a multiple of 8, XCD x takes heads [x H/8, (x+1) H/8) of
-// every sequence (balanced even when packed sequences differ in length) and
-// walks them tile-major, so the tiles it streams stay in its own L2; else,
-// when B*H is, it takes the x-th contiguous slice of the (b, head) rows;
-// else the whole grid is walked tile-major.
-__device__ __forceinline__ void bwd_item(int B, int H, int& b, int& h, int& tile) {
-  const int i = (int)blockIdx.x, xcd = i % 8, slot = i / 8;
-  const int rows = B * H;
-  int row;
-  if (H % 8 == 0) {
-    const int hx = H / 8, per = B * hx;
-    tile = slot / per;
-    const int r = slot - tile * per;
-    b = r / hx;
-    h = xcd * hx + (r - b * hx);
-    return;
-  } else if (rows % 8 == 0) {
-    const int per = rows / 8;
-    tile = slot / per;
-    row = xcd * per + (slot - tile * per);
-  } else {
-    tile = i / rows;
-    row = i - tile * rows;
-  }
-  b = row / H;
-  h = row - b * H;
-}
-
 // LDS-direct copy of `rows` x D 16-bit elements (rows r0 .. r0+rows-1 of a
 // matrix with row stride `stride` elements; rows past `last` re-read `last`)
 // into an LDS tile, 16-byte chunks XOR-swizzled by row.  Every thread of the
@@ -305,7 +274,7 @@ void bwd_dq_kernel(const BwdParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int nqt = (p.Lq + kBM - 1) / kBM;
   int b, h, tt;
-  bwd_item(p.B, Hq, b, h, tt);
+  bwd_item((int)blockIdx.x, p.B, Hq, b, h, tt);
   const int qt = CAUSAL ? nqt - 1 - tt : tt;  // heaviest (last, under a causal mask) first
   const SeqRows sr = seq_rows(p, b);
   const int Lq = sr.Lq, Lk = sr.Lk;
@@ -529,7 +498,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const bool sw = ((wu & 1) ^ ((wu >> 2) & 1)) != 0;
   // Key tiles ascending: under a causal mask the first see the most queries.
   int b, kvh, kt;
-  bwd_item(p.B, Hkv, b, kvh, kt);
+  bwd_item((int)blockIdx.x, p.B, Hkv, b, kvh, kt);
   const SeqRows sr = seq_rows(p, b);
   const int Lq = sr.Lq, Lk = sr.Lk;
   const int k0 = kt * KBM;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_sched.hpp"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -134,41 +136,5 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-
-// Block -> (sequence b, query head h, query-tile rank) for the forward
-// kernels.  Blocks are dealt to the 8 XCDs round-robin (block i runs on XCD
-// i % 8, each XCD with its own L2) and start in index order.  When Hq is a
-// multiple of 8, XCD x takes query heads [x*Hq/8, (x+1)*Hq/8) of every
-// sequence, which balances the XCDs even when packed sequences differ in
-// length.  Its rows (sequence, head) are walked in windows of W adjacent rows,
-// rank-major within a window (rank 0 of each row, then rank 1, ...): the heavy
-// ranks of every window start together and the grid ends on light blocks,
-// while the few rows of a window keep their K/V tiles in L2.  W (from
-// xcd_window) is a multiple of gx = gcd(Hq/Hkv, Hq/8), so the heads reading
-// one K/V head run side by side.  Otherwise XCD x takes the x-th contiguous
-// slice of the (sequence, head, rank) list.  The caller maps rank to a query
-// tile (heaviest first).
-__device__ __forceinline__ void xcd_work_item(int B, int Hq, int nqt, int W, int& b, int& h,
-                                              int& rank) {
-  constexpr int kXcd = 8;
-  const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
-  if (Hq % kXcd == 0) {
-    const int hx = Hq / kXcd, rows = B * hx;
-    const int wi = slot / (W * nqt);
-    const int w0 = wi * W, wn = min(W, rows - w0);
-    const int r = slot - wi * W * nqt;
-    rank = r / wn;
-    const int row = w0 + (r - rank * wn);
-    b = row / hx;
-    h = xcd * hx + (row - b * hx);
-  } else {
-    const int N = nqt * B * Hq;
-    const int item = xcd * (N / kXcd) + min(xcd, N % kXcd) + slot;
-    const int bhi = item / nqt;
-    rank = item - bhi * nqt;
-    b = bhi / Hq;
-    h = bhi - b * Hq;
-  }
-}
 
 }  // namespace fa

@@ -155,7 +155,7 @@ void fwd_kernel(const FwdParams prm) {
 
   const int nqt = (prm.Lq + BM - 1) / BM;
   int b, h, qt;
-  xcd_work_item(B, Hq, nqt, prm.xcd_w, b, h, qt);
+  xcd_work_item((int)blockIdx.x, B, Hq, nqt, prm.xcd_w, b, h, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
   const int bh = b * Hq + h;
   const int kvh = h / (Hq / Hkv);
@@ -173,19 +173,13 @@ void fwd_kernel(const FwdParams prm) {
   }
   const int q0 = qt * BM;
   if (q0 >= Lq) return;  // past this sequence's rows (whole workgroup)
-  const int shift = Lk - Lq;
   const int qw0 = q0 + kFwdRowsPerWave * w;
   const int qrow = qw0 + l32;
 
   // Keys row i may see: [kmin(i), kmax(i)], both non-decreasing in i.
-  const int wl = prm.win_left, wr = prm.win_right;
-  auto kmin = [&](int i) { return wl < 0 ? 0 : max(0, i + shift - wl); };
-  auto kmax = [&](int i) {
-    int hi = Lk - 1;
-    if (CAUSAL) hi = min(hi, i + shift);
-    if (wr >= 0) hi = min(hi, i + shift + wr);
-    return hi;
-  };
+  const KeyRange kr(Lq, Lk, CAUSAL, prm.win_left, prm.win_right);
+  auto kmin = [&](int i) { return kr.kmin(i); };
+  auto kmax = [&](int i) { return kr.kmax(i); };
 
   const long qstride = (long)Hq * D;
   const long kstride = (long)Hkv * D;
@@ -196,9 +190,9 @@ void fwd_kernel(const FwdParams prm) {
   // Tiles t_first .. t_first+ntiles-1 hold every key some row of the
   // workgroup sees; below, u = t - t_first indexes them.
   const int q_last = min(q0 + BM, Lq) - 1;
-  const int wg_lo = kmin(q0), wg_hi = kmax(q_last);
-  const int t_first = wg_lo / BN;
-  const int ntiles = wg_hi >= wg_lo ? wg_hi / BN - t_first + 1 : 0;
+  const FwdWalk walk(kr, q0, q_last, BN);
+  const int t_first = walk.t_first;
+  const int ntiles = walk.ntiles;
 
   // Loader: load i of this thread fills 16-byte chunk position P of the tile
   // (row P / CPR, stored chunk P % CPR holding logical chunk (P % CPR) ^ swz).
@@ -393,8 +387,9 @@ void fwd_kernel(const FwdParams prm) {
   // S(t+1), P(t) and P(t) V(t) (S first, so its MFMAs overlap the exponentials;
   // the acceptance test of P(t) comes before the PV MFMAs that read it).  In
   // the main phase (TAIL false) tiles t and t+1 are fully visible to every row
-  // of the workgroup, so nothing is masked or skipped.
-  auto step = [&](int t, auto I, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32], auto tail_tag) {
+  // of the workgroup and the copies lie whole inside the keys (FwdWalk), so
+  // nothing is masked, skipped or clamped.
+  auto step_sc = [&](int t, auto I, f32x16 (&sc)[BN / 32], f32x16 (&sn)[BN / 32], auto tail_tag) {
     constexpr int i = decltype(I)::value;
     constexpr bool TAIL = decltype(tail_tag)::value;
     using Inext = std::integral_constant<int, (i + 1) % kStages>;
@@ -426,18 +421,17 @@ void fwd_kernel(const FwdParams prm) {
       pv(pk, vst(I));
     }
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
+  // Score tiles alternate: even steps hold S(t) in sA, odd ones in sB.
+  f32x16 sA[BN / 32], sB[BN / 32];
+  auto step = [&](int t, auto I, auto tail_tag) {
+    if constexpr (decltype(I)::value % 2 == 0)
+      step_sc(t, I, sA, sB, tail_tag);
+    else
+      step_sc(t, I, sB, sA, tail_tag);
+  };
   using S2 = std::integral_constant<int, 2 % kStages>;
   using S3 = std::integral_constant<int, 3 % kStages>;
 
-  // Relative tiles [m_lo, m_hi) are seen whole by every row of the workgroup.
-  const int m_lo = max(0, (kmin(q_last) + BN - 1) / BN - t_first);
-  const int m_hi = min(ntiles, (kmax(q0) + 1) / BN - t_first);
-  using Main = std::integral_constant<bool, false>;
-  using Tail = std::integral_constant<bool, true>;
-
-  f32x16 sA[BN / 32], sB[BN / 32];
   if (ntiles > 0) {
     // Prologue: K(0), then (K(j), V(j-1)) for j = 1 .. kStages-1.
     issue_k(0, sK0);
@@ -454,49 +448,12 @@ void fwd_kernel(const FwdParams prm) {
       scores(sA, sK0);
       mask(sA, 0);
     }
-    // Every phase walks kStages tiles at a time from t = 0, so stages and
-    // score arrays are in the same roles at every loop head.
-    int t = 0;
-    // Head phase (windows): masked tiles before the whole ones.  Running out
-    // of tiles here ends the walk (t = ntiles skips the later phases).
-    const int m_lo_al = (m_lo + kStages - 1) / kStages * kStages;
-    while (t < m_lo_al && t < ntiles) {
-      step(t, S0{}, sA, sB, Tail{});
-      if (t + 1 >= ntiles) { t = ntiles; break; }
-      step(t + 1, S1{}, sB, sA, Tail{});
-      if constexpr (kStages > 2) {
-        if (t + 2 >= ntiles) { t = ntiles; break; }
-        step(t + 2, S2{}, sA, sB, Tail{});
-        if (t + 3 >= ntiles) { t = ntiles; break; }
-        step(t + 3, S3{}, sB, sA, Tail{});
-      }
-      t += kStages;
-    }
-    // Main phase: step t runs unmasked when tiles t and t+1 are both whole.
-    kp = Kb + (long)(t_first + t + kStages) * tstride;
-    vp = Vb + (long)(t_first + t + kStages - 1) * tstride;
-    while (t >= m_lo && t + kStages < m_hi) {
-      step(t, S0{}, sA, sB, Main{});
-      step(t + 1, S1{}, sB, sA, Main{});
-      if constexpr (kStages > 2) {
-        step(t + 2, S2{}, sA, sB, Main{});
-        step(t + 3, S3{}, sB, sA, Main{});
-      }
-      t += kStages;
-    }
-    // Tail phase: masked or partly skipped tiles (and the last whole ones).
-    while (t < ntiles) {
-      step(t, S0{}, sA, sB, Tail{});
-      if (t + 1 >= ntiles) break;
-      step(t + 1, S1{}, sB, sA, Tail{});
-      if constexpr (kStages > 2) {
-        if (t + 2 >= ntiles) break;
-        step(t + 2, S2{}, sA, sB, Tail{});
-        if (t + 3 >= ntiles) break;
-        step(t + 3, S3{}, sB, sA, Tail{});
-      }
-      t += kStages;
-    }
+    // Head phase (masked tiles left of some row's window), main phase
+    // (unmasked, running tile pointers), tail phase (masked or partly skipped).
+    fwd_walk<kStages>(walk, step, [&](int t) {
+      kp = Kb + (long)(t_first + t + kStages) * tstride;
+      vp = Vb + (long)(t_first + t + kStages - 1) * tstride;
+    });
   }
   wait_vmem();  // copies of re-read tiles past the end are still landing
 

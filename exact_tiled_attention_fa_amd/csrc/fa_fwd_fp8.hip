@@ -107,7 +107,7 @@ void fwd_fp8_kernel(const Fp8Params prm) {
 
   const int nqt = (prm.Lq + kPBM - 1) / kPBM;
   int b, h, qt;
-  xcd_work_item(B, Hq, nqt, prm.xcd_w, b, h, qt);
+  xcd_work_item((int)blockIdx.x, B, Hq, nqt, prm.xcd_w, b, h, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int kvh = h / (Hq / Hkv);
   // This sequence's rows.  Packed offsets are clamped into the tensors so

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa_sched.hpp"
+
 namespace fa {
 
 struct FwdArgs {
@@ -23,26 +25,6 @@ struct FwdArgs {
   const int* cu_k = nullptr;
   int total_q = 0, total_k = 0;       // packed row counts
 };
-
-// Window W of xcd_work_item (device side, fa_common.hpp): the smallest
-// multiple of gx = gcd(Hq/Hkv, Hq/8) that divides the B*Hq/8 rows of an XCD
-// and spans at least twice the blocks the XCD holds at once (32 CUs x
-// blocks_per_cu), so that each window's heavy ranks start early; the whole
-// row list if none does.  1 when Hq is not a multiple of 8 (unused there).
-inline int xcd_window(int B, int Hq, int Hkv, int nqt, int blocks_per_cu) {
-  if (Hq % 8 != 0) return 1;
-  const int hx = Hq / 8, rows = B * hx;
-  int gx = Hq / Hkv, m = hx;  // gcd
-  while (m != 0) {
-    const int t = gx % m;
-    gx = m;
-    m = t;
-  }
-  const int want = (2 * 32 * blocks_per_cu + nqt - 1) / nqt;
-  for (int w = gx; w < rows; w += gx)
-    if (w >= want && rows % w == 0) return w;
-  return rows;
-}
 
 struct DecodeArgs {
   const void* q;
@@ -111,14 +93,6 @@ size_t bwd_workspace_bytes(int B, int Hq, int Lq);
 int bwd_padded_rows(int Lq);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
-
-// Matrix-core ceiling probe (a measurement helper): nblocks workgroups of
-// mfma_probe_threads(1) threads over n16 16-byte operands; out holds one float
-// per thread.
-hipError_t launch_mfma_probe(const void* ops, long n16, float* out, int nblocks, int iters,
-                             hipStream_t stream);
-double mfma_probe_flops(int nblocks, int iters);
-int mfma_probe_threads(int nblocks);
 
 // Prefill tiling, reported by fa_info().
 #ifndef FA_FWD_WAVES
