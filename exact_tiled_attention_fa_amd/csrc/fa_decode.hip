@@ -451,7 +451,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   p.S = a.num_splits;
   // |scale| * log2(e), kept >= 1e-30 so masked (-inf) scores give probability 0.
   p.scale2 = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
-  p.thr = 8.f / p.scale2;
+  // The running max moves only when a score exceeds it by more than thr, so
+  // probabilities reach at most 2^8.  With fp16 and int8 values each
+  // probability is multiplied by its value row's scale before the 16-bit
+  // rounding; there the max moves at once (p <= 1), so p * scale stays within
+  // fp16 wherever the dequantised values themselves fit it (|code| * scale
+  // <= 127 * scale, the same bound the output needs).
+  p.thr = (VI8 && std::is_same<T, f16_t>::value) ? 0.f : 8.f / p.scale2;
   p.qxor = (a.scale < 0.f) ? 0x80008000u : 0u;
   hipLaunchKernelGGL((decode_split_kernel<T, D, PAGED, KI8, VI8>), dim3(a.num_splits, a.Hkv * nhg, a.B),
                      dim3(64 * kDW), 0, stream, p);
