@@ -151,6 +151,22 @@ def _default_workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
+def run_jobs(fn, jobs, workers):
+    """fn(job) for every job: in order on this thread when workers <= 1,
+    else in a thread pool of ``workers`` threads (None: the host's core
+    count) with BLAS held to one thread per worker.  The jobs write disjoint
+    slices of their outputs, so the order does not matter."""
+    nw = workers if workers is not None else _default_workers()
+    if nw <= 1 or len(jobs) <= 1:
+        for j in jobs:
+            fn(j)
+        return
+    import contextlib
+    ctx = threadpool_limits(limits=1) if threadpool_limits is not None else contextlib.nullcontext()
+    with ctx, ThreadPoolExecutor(max_workers=nw) as ex:
+        list(ex.map(fn, jobs))
+
+
 def attention_ref(q, k, v, scale: float, causal: bool, *, row_block: int = 1024,
                   workers: int | None = None, heads=None, window=(-1, -1)):
     """Plain fp64 attention.
@@ -186,26 +202,19 @@ def attention_ref(q, k, v, scale: float, causal: bool, *, row_block: int = 1024,
         out[b, :, h, :] = o
         lse[b, h, :] = l
 
-    nw = workers if workers is not None else _default_workers()
-    if nw <= 1 or len(jobs) <= 1:
-        for j in jobs:
-            run(j)
-    else:
-        import contextlib
-        ctx = threadpool_limits(limits=1) if threadpool_limits is not None else contextlib.nullcontext()
-        with ctx, ThreadPoolExecutor(max_workers=nw) as ex:
-            list(ex.map(run, jobs))
+    run_jobs(run, jobs, workers)
     return out, lse
 
 
-def decode_ref(q, k_cache, v_cache, seqlens, scale: float, *, heads=None):
+def decode_ref(q, k_cache, v_cache, seqlens, scale: float, *, heads=None, workers: int | None = 1):
     """One query token per sequence against a padded KV cache.
 
     q: [B, Hq, D]; k_cache, v_cache: [B, Lk_max, Hkv, D]; seqlens: [B] ints.
     Sequence b attends to keys 0 .. seqlens[b]-1 (all of them: the query is
     the newest token, so the bottom-right causal mask admits its whole
     cache).  Padding rows beyond seqlens[b] are never read.  Returns
-    (O [B, Hq, D], lse [B, Hq]) in float64.
+    (O [B, Hq, D], lse [B, Hq]) in float64.  ``workers`` > 1 runs the
+    sequences in a thread pool (None: the host's core count).
     """
     q = _as_f64(q)
     B, Hq, D = q.shape
@@ -217,18 +226,24 @@ def decode_ref(q, k_cache, v_cache, seqlens, scale: float, *, heads=None):
     out = np.full((B, Hq, v_cache.shape[3]), np.nan)
     lse = np.full((B, Hq), np.nan)
     jobs = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
-    cache_k, cache_v = {}, {}
+    by_seq = {}
     for b, h in jobs:
-        kv = h // g
+        by_seq.setdefault(b, []).append(h)
+
+    def run(b):
         n = max(0, min(lens[b], k_cache.shape[1]))
-        key = (b, kv)
-        if key not in cache_k:  # slice first: padding (possibly NaN) is never touched
-            cache_k[key] = _as_f64(k_cache[b, :n, kv, :])
-            cache_v[key] = _as_f64(v_cache[b, :n, kv, :])
-        o, l = _head_attention(q[b, h, :][None, :], cache_k[key], cache_v[key],
-                               float(scale), False, 1)
-        out[b, h, :] = o[0]
-        lse[b, h] = l[0]
+        cache_k, cache_v = {}, {}
+        for h in by_seq[b]:
+            kv = h // g
+            if kv not in cache_k:  # slice first: padding (possibly NaN) is never touched
+                cache_k[kv] = _as_f64(k_cache[b, :n, kv, :])
+                cache_v[kv] = _as_f64(v_cache[b, :n, kv, :])
+            o, l = _head_attention(q[b, h, :][None, :], cache_k[kv], cache_v[kv],
+                                   float(scale), False, 1)
+            out[b, h, :] = o[0]
+            lse[b, h] = l[0]
+
+    run_jobs(run, list(by_seq), workers)
     return out, lse
 
 
@@ -247,7 +262,7 @@ def _paged_rows(pages, scales, rows_page, rows_slot, kv):
 
 
 def decode_paged_ref(q, k_pages, v_pages, block_table, seqlens, scale: float, *, k_scales=None,
-                     v_scales=None, heads=None):
+                     v_scales=None, heads=None, workers: int | None = 1):
     """One query token per sequence against a paged, optionally int8, cache.
 
     q: [B, Hq, D]; k_pages, v_pages: [num_pages, P, Hkv, D]; block_table:
@@ -257,6 +272,8 @@ def decode_paged_ref(q, k_pages, v_pages, block_table, seqlens, scale: float, *,
     k_pages holds integer codes and the cached key is code * scale (exact in
     float64); likewise v_scales for the values.  Then the definition of
     ``decode_ref``.  Returns (O [B, Hq, D], lse [B, Hq]) in float64.
+    ``workers`` > 1 runs the sequences in a thread pool (None: the host's
+    core count).
     """
     q = _as_f64(q)
     B, Hq, D = q.shape
@@ -269,19 +286,26 @@ def decode_paged_ref(q, k_pages, v_pages, block_table, seqlens, scale: float, *,
     out = np.full((B, Hq, int(v_pages.shape[3])), np.nan)
     lse = np.full((B, Hq), np.nan)
     jobs = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
-    cache = {}
+    by_seq = {}
     for b, h in jobs:
-        kv = h // g
-        if (b, kv) not in cache:
-            n = max(0, min(lens[b], bt.shape[1] * P))
-            j = np.arange(n)
-            page, slot = bt[b, j // P], j % P
-            cache[(b, kv)] = (_paged_rows(k_pages, k_scales, page, slot, kv),
-                              _paged_rows(v_pages, v_scales, page, slot, kv))
-        kb, vb = cache[(b, kv)]
-        o, l = _head_attention(q[b, h, :][None, :], kb, vb, float(scale), False, 1)
-        out[b, h, :] = o[0]
-        lse[b, h] = l[0]
+        by_seq.setdefault(b, []).append(h)
+
+    def run(b):
+        n = max(0, min(lens[b], bt.shape[1] * P))
+        j = np.arange(n)
+        page, slot = bt[b, j // P], j % P
+        cache = {}
+        for h in by_seq[b]:
+            kv = h // g
+            if kv not in cache:
+                cache[kv] = (_paged_rows(k_pages, k_scales, page, slot, kv),
+                             _paged_rows(v_pages, v_scales, page, slot, kv))
+            kb, vb = cache[kv]
+            o, l = _head_attention(q[b, h, :][None, :], kb, vb, float(scale), False, 1)
+            out[b, h, :] = o[0]
+            lse[b, h] = l[0]
+
+    run_jobs(run, list(by_seq), workers)
     return out, lse
 
 

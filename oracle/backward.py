@@ -43,7 +43,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import _as_f64, row_bounds
+from .attention import _as_f64, row_bounds, run_jobs
 
 
 def _head_backward(qh, kh, vh, doh, scale, causal, window, row_block, bounds):
@@ -91,7 +91,8 @@ def _head_backward(qh, kh, vh, doh, scale, causal, window, row_block, bounds):
 
 
 def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, *, window=(-1, -1),
-                      kv_heads=None, row_block: int = 512, bounds: bool = False):
+                      kv_heads=None, row_block: int = 512, bounds: bool = False,
+                      workers: int | None = 1):
     """Gradients of ``attention_ref``'s O with respect to q, k, v, given dO.
 
     q, do: [B, Lq, Hq, D]; k, v: [B, Lk, Hkv, D].  Returns (dq, dk, dv) in
@@ -99,7 +100,9 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, *, window=(-1, -1
     abs_dv), the per-element sums of |terms| of each gradient (for error
     bounds).  ``kv_heads`` optionally restricts the work to a list of
     (b, kv head) pairs: their dK, dV and the dQ of their query heads are
-    computed, everything else is NaN.
+    computed, everything else is NaN.  ``workers`` > 1 runs the (b, kv head)
+    pairs in a thread pool (BLAS held to one thread per worker); None picks
+    the host's core count.
 
     The bounds are abs_dv_j = sum_i P_ij |dO_i|, abs_dq_i = |scale| sum_j
     w_ij |k_j| and abs_dk_j = |scale| sum_i w_ij |q_i| with w_ij = |dS_ij| +
@@ -118,7 +121,8 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, *, window=(-1, -1
     absd = [np.full(x.shape, np.nan) for x in out] if bounds else None
     jobs = list(kv_heads) if kv_heads is not None else [(b, c) for b in range(B)
                                                           for c in range(Hkv)]
-    for b, c in jobs:
+    def run(job):
+        b, c = job
         dk_acc = np.zeros((Lk, D))
         dv_acc = np.zeros((Lk, v.shape[3]))
         ak_acc = np.zeros((Lk, D))
@@ -139,20 +143,22 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, *, window=(-1, -1
         if bounds:
             absd[1][b, :, c] = ak_acc
             absd[2][b, :, c] = av_acc
+
+    run_jobs(run, jobs, workers)
     if bounds:
         return tuple(out) + tuple(absd)
     return tuple(out)
 
 
 def varlen_bwd_ref(q, k, v, do, cu_q, cu_k, scale: float, causal: bool, *, window=(-1, -1),
-                   kv_heads=None, bounds: bool = False):
+                   kv_heads=None, bounds: bool = False, workers: int | None = 1):
     """Gradients of ``varlen_ref``'s O: sequence b is rows cu_q[b] ..
     cu_q[b+1]-1 of q, do [total_q, Hq, D] and rows cu_k[b] .. cu_k[b+1]-1 of
     k, v [total_k, Hkv, D].  Returns (dq, dk, dv) in float64 with the shapes
     of q, k, v (and, with ``bounds``, the |term| sums of attention_bwd_ref).
     Keys of a sequence that no query row sees get dk = dv = 0.  ``kv_heads``
     optionally restricts the work to (b, kv head) pairs; everything else is
-    NaN."""
+    NaN.  ``workers``: the thread pool of attention_bwd_ref, per sequence."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
     cu_q = [int(x) for x in np.asarray(cu_q).reshape(-1)]
     cu_k = [int(x) for x in np.asarray(cu_k).reshape(-1)]
@@ -166,7 +172,8 @@ def varlen_bwd_ref(q, k, v, do, cu_q, cu_k, scale: float, causal: bool, *, windo
         if sel is not None and not sel:
             continue
         res = attention_bwd_ref(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], do[None, q0:q1],
-                                scale, causal, window=window, kv_heads=sel, bounds=bounds)
+                                scale, causal, window=window, kv_heads=sel, bounds=bounds,
+                                workers=workers)
         cs = range(Hkv) if sel is None else [c for _, c in sel]
         for c in cs:
             hs = slice(c * g, (c + 1) * g)

@@ -100,20 +100,19 @@ def test_bwd_d256_gqa_window(gpu):
     check(1, 300, 300, 4, 1, 256, torch.bfloat16, False, seed=82, gpu=gpu, window=(40, 9))
 
 
-def test_bwd_d256_full_size_sampled(gpu):
+def test_bwd_d256_full_size(gpu):
     """The d256 workload (B=2, H=16, L=4096, D=256, fp16, causal); the oracle
-    computes two whole heads' gradients."""
+    computes every head's gradients."""
     cfg = W.PREFILL["d256"]
     q, k, v = W.prefill_inputs(cfg)
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(cfg.seed + 100)).to(cfg.dtype)
     scale = f32(cfg.scale)
     say("bwd full-size d256")
     dq, dk, dv = run_bwd(q, k, v, do, scale, True, (-1, -1), gpu)
-    heads = [(0, 0), (cfg.B - 1, cfg.Hkv - 1)]
-    r = oracle.attention_bwd_ref(q, k, v, do, scale, True, bounds=True, kv_heads=heads)
-    compare_grad(dq, r[0], r[3], cfg.dtype, f"dq {heads}")
-    compare_grad(dk, r[1], r[4], cfg.dtype, f"dk {heads}")
-    compare_grad(dv, r[2], r[5], cfg.dtype, f"dv {heads}")
+    r = oracle.attention_bwd_ref(q, k, v, do, scale, True, bounds=True, workers=16)
+    compare_grad(dq, r[0], r[3], cfg.dtype, "dq all heads")
+    compare_grad(dk, r[1], r[4], cfg.dtype, "dk all heads")
+    compare_grad(dv, r[2], r[5], cfg.dtype, "dv all heads")
 
 
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
@@ -203,21 +202,22 @@ def test_bwd_offsets_past_2_31(gpu):
     compare_grad(first[2], r[2], r[5], torch.bfloat16, f"dv {heads}")
 
 
-def test_bwd_full_size_sampled(gpu):
+def test_bwd_full_size(gpu):
     """The Llama-2-7B-shaped causal workload (B=4, H=32, L=4096, D=128, bf16)
-    in the launch the benchmark times; the oracle computes two whole K/V
-    heads' gradients (the first and the last)."""
+    in the launch the benchmark times; the oracle computes the gradients of
+    every head of the first and of the last batch entry."""
     cfg = W.PREFILL["llama7b"]
     q, k, v = W.prefill_inputs(cfg)
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(cfg.seed + 100)).to(cfg.dtype)
     scale = f32(cfg.scale)
     say("bwd full-size llama7b")
     dq, dk, dv = run_bwd(q, k, v, do, scale, True, (-1, -1), gpu)
-    heads = [(0, 0), (cfg.B - 1, cfg.Hkv - 1)]
-    r = oracle.attention_bwd_ref(q, k, v, do, scale, True, bounds=True, kv_heads=heads)
-    compare_grad(dq, r[0], r[3], cfg.dtype, f"dq {heads}")
-    compare_grad(dk, r[1], r[4], cfg.dtype, f"dk {heads}")
-    compare_grad(dv, r[2], r[5], cfg.dtype, f"dv {heads}")
+    heads = [(b, c) for b in (0, cfg.B - 1) for c in range(cfg.Hkv)]
+    r = oracle.attention_bwd_ref(q, k, v, do, scale, True, bounds=True, kv_heads=heads,
+                                 workers=16)
+    compare_grad(dq, r[0], r[3], cfg.dtype, "dq batch entries 0 and 3")
+    compare_grad(dk, r[1], r[4], cfg.dtype, "dk batch entries 0 and 3")
+    compare_grad(dv, r[2], r[5], cfg.dtype, "dv batch entries 0 and 3")
 
 
 def test_bwd_errors(gpu):

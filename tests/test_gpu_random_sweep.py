@@ -29,6 +29,12 @@ def draw_window(rng):
 
 
 def draw_heads(rng):
+    """Small head counts, or (about a third of the draws) 16 to 64 query
+    heads in multiples of 8, where the forward deals heads to the XCDs in
+    windows (several heads per XCD) and the backward walks heads per XCD."""
+    if rng.random() < 0.35:
+        Hkv = int(rng.choice([2, 4, 8]))
+        return Hkv * int(rng.choice([2, 4, 8])) if Hkv < 8 else 8 * int(rng.choice([2, 4, 8])), Hkv
     Hkv = int(rng.choice([1, 2, 3]))
     return Hkv * int(rng.choice([1, 2, 4, 5])), Hkv
 
