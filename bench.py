@@ -13,14 +13,22 @@ on the stream the kernel runs on; the decode half is reported in the same
 line as algorithmic HBM GB/s (K/V rows of each cache read once, q read, o and
 lse written).  ``ms_per_step`` is wall time per step over the K timed steps.
 
-The structured-mask prefill workloads (sliding window ``swa16k``, packed
-sequences ``varlen16``) are timed after the step loop, with HIP events around
-each launch, and reported under ``masks`` in the same line; they are not part
-of ``value``.
+Before the W warm-up steps the step is repeated untimed for ``--settle``
+seconds (``settle_s`` in the line): the GPU clocks take ~100 ms of load to
+ramp up after an idle spell, and a few warm-up steps do not cover that.  The
+graphics clock under the step's load is read from amd-smi after the timed
+region (``sclk``).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--with-copy MIB] [--only prefill|decode] [--no-masks]
-                    [--all-configs]
+The other prefill workloads are timed after the step loop, each launch with
+its own HIP event pair, and reported under ``configs``: the long-context GQA
+prefill, the D=256 prefill, the bidirectional encoder (cold: a 512 MiB buffer
+is written between launches, outside the timed region, so that its inputs
+are not served from the 256 MiB last-level cache) and the tiny case (µs).
+The paged / int8 decode, FP8 forward, backward and structured-mask workloads
+follow under their own keys.  None of them is part of ``value``.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--settle SECONDS]
+                    [--no-cpu-baseline] [--probe] [--only ...]
 """
 
 from __future__ import annotations
@@ -48,20 +56,30 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--settle", type=float, default=2.0,
+                   help="seconds of untimed steps before the warm-up (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--with-copy", type=int, default=0, metavar="MIB",
                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
-    p.add_argument("--only", choices=["prefill", "decode", "masks", "paged", "bwd", "fp8"],
+    p.add_argument("--only", choices=["prefill", "decode", "masks", "paged", "bwd", "fp8",
+                                      "config"],
                    default=None,
-                   help="masks / paged / bwd: time only the structured-mask prefill, the paged "
-                        "decode or the backward workloads (one JSON line)")
+                   help="time only this part (one JSON line); config: one prefill workload "
+                        "named by --config")
+    p.add_argument("--config", default=None, help="with --only config: the prefill workload")
+    p.add_argument("--reps", type=int, default=None,
+                   help="launches per side measurement (default: per workload)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other prefill workloads (long-context, D=256, encoder, tiny)")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward workload")
     p.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward workload")
-    p.add_argument("--no-probe", action="store_true",
-                   help="skip the matrix-core ceiling probe on the prefill's operands")
+    p.add_argument("--probe", action="store_true",
+                   help="also time the matrix-core probe (libfa_probe.so) on the prefill's Q "
+                        "and on constant operands")
+    p.add_argument("--no-sclk", action="store_true", help="do not read the clock from amd-smi")
     p.add_argument("--paged-format", choices=["native", "k8", "kv8"], default=None,
                    help="time only this paged-cache format")
     p.add_argument("--no-paged", action="store_true",
@@ -69,8 +87,6 @@ def parse():
     p.add_argument("--mask", default=None, help="time only this structured-mask workload")
     p.add_argument("--no-masks", action="store_true",
                    help="skip the structured-mask prefill workloads (sliding window, packed)")
-    p.add_argument("--all-configs", action="store_true",
-                   help="also print one extra JSON line per prefill workload")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script with "
                         "--with-copy (FETCH_SIZE, then WRITE_SIZE) into profiles/traffic.json")
@@ -169,7 +185,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> di
 
 
 def cpu_baseline_prefill(cfg, q, k, v, scale, target_s):
-    """Time the fp64 oracle on a bounded sample of whole (batch, head) slices."""
+    """Time the fp64 oracle on a bounded sample of whole (batch, head) slices
+    (all of them when they fit in about target_s seconds)."""
     import oracle
     from oracle.attention import _default_workers
 
@@ -186,26 +203,38 @@ def cpu_baseline_prefill(cfg, q, k, v, scale, target_s):
     oracle.attention_ref(q, k, v, scale, cfg.causal, heads=pairs[:n], workers=workers)
     dt = time.perf_counter() - t0
     return {"value": round(per_head_flops * n / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": workers, "kind": "oracle",
+            "cores": workers, "kind": "oracle", "host": host_cpu(),
             "sample": f"{n} of {len(pairs)} (batch, head) slices of the same workload, "
                       f"fp64 numpy, {dt:.2f} s wall"}
 
 
-def cpu_baseline_decode(cfg, q, kc, vc, lens, scale, nseq=16):
+def cpu_baseline_decode(cfg, q, kc, vc, lens, scale):
+    """The fp64 oracle's decode on the whole decode workload (every sequence
+    and head), one thread per sequence over the host's cores."""
     import oracle
+    from oracle.attention import _default_workers
+
+    workers = _default_workers()
+    t0 = time.perf_counter()
+    oracle.decode_ref(q, kc, vc, lens, scale, workers=workers)
+    dt = time.perf_counter() - t0
     from exact_tiled_attention_fa_amd import workloads as W
+    byts = W.decode_bytes(cfg, lens)
+    return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "host": host_cpu(),
+            "sample": f"all {cfg.B} sequences x {cfg.Hq} heads of the same workload, fp64 numpy, "
+                      f"{dt:.2f} s wall"}
 
-    from threadpoolctl import threadpool_limits
 
-    heads = [(b, h) for b in range(nseq) for h in range(cfg.Hq)]
-    with threadpool_limits(limits=1):  # the oracle's decode is one thread; so is its BLAS
-        t0 = time.perf_counter()
-        oracle.decode_ref(q, kc, vc, lens, scale, heads=heads)
-        dt = time.perf_counter() - t0
-    sub = lens[:nseq]
-    byts = int(sum(int(x) for x in sub)) * cfg.Hkv * cfg.D * 2 * 2 + nseq * cfg.Hq * (2 * cfg.D * 2 + 4)
-    return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {nseq} of {cfg.B} sequences, all heads, fp64 numpy, {dt:.2f} s wall"}
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return f"{line.split(':', 1)[1].strip()} ({os.cpu_count()} logical CPUs)"
+    except OSError:
+        pass
+    return f"{os.cpu_count()} logical CPUs"
 
 
 def copy_calibration(mib, dev):
@@ -228,21 +257,164 @@ PAGE_SIZE = 16
 def settle(run, seconds=0.25):
     """Untimed: repeat run() for `seconds` of wall time so that the GPU clocks
     have ramped up before a measurement (a few calls are not enough; the first
-    ~100 ms of work after idle run 10-20 % slow)."""
+    ~100 ms of work after idle run 10-20 % slow).  Returns the number of
+    calls."""
     import torch
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    n = 0
     while time.perf_counter() - t0 < seconds:
         for _ in range(4):
             run()
+        n += 4
         torch.cuda.synchronize()
+    return n
 
 
-def time_paged(fmt, dev, reps=10):
+def ms_stats(ms):
+    import numpy as np
+
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "min": round(float(a.min()), 5), "p90": round(float(np.percentile(a, 90)), 5),
+            "n": int(a.size)}
+
+
+def time_launches(run, reps, between=None):
+    """Per-launch times (ms) of run(), each bracketed by its own HIP event
+    pair on the current stream (the stream the library launches on).
+    between(), if given, runs before each launch outside its event pair."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        if between is not None:
+            between()
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def sclk_under_load(run, timeout_s=20.0):
+    """The graphics clock (MHz) amd-smi reports while run() keeps the GPU busy:
+    amd-smi runs as a child process and the step is repeated until it ends."""
+    import subprocess
+
+    import torch
+
+    cmds = [["amd-smi", "metric", "-g", "0", "-c", "--json"],
+            ["rocm-smi", "-d", "0", "--showclocks", "--json"]]
+    for cmd in cmds:
+        try:
+            proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                                    text=True)
+        except OSError:
+            continue
+        t0 = time.perf_counter()
+        while proc.poll() is None and time.perf_counter() - t0 < timeout_s:
+            for _ in range(4):
+                run()
+            torch.cuda.synchronize()
+        try:
+            out, _ = proc.communicate(timeout=max(1.0, timeout_s - (time.perf_counter() - t0)))
+        except subprocess.TimeoutExpired:
+            proc.kill()
+            proc.communicate()
+            continue
+        mhz = _parse_sclk(out)
+        if mhz:
+            return {"mhz_mean": round(sum(mhz) / len(mhz), 1), "mhz_min": min(mhz),
+                    "mhz_max": max(mhz), "readings": len(mhz), "tool": cmd[0]}
+    return None
+
+
+def _parse_sclk(text):
+    """Graphics-clock readings (MHz) in amd-smi / rocm-smi JSON output (amd-smi
+    gives one per XCD)."""
+    import re
+
+    try:
+        data = json.loads(text)
+    except ValueError:
+        return None
+    found = []
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            for k, v in x.items():
+                walk(v, path + [str(k).lower()])
+        elif isinstance(x, list):
+            for v in x:
+                walk(v, path)
+        else:
+            p = "/".join(path)
+            gfx = re.search(r"gfx_\d+/clk(/value)?$", p) or re.search(r"sclk clock speed", p)
+            if gfx:
+                m = re.search(r"(\d+(\.\d+)?)", str(x))
+                if m:
+                    found.append(float(m.group(1)))
+
+    walk(data, [])
+    return found or None
+
+
+def time_prefill_cfg(name, dev, reps=50, cold=False):
+    """One prefill workload: per-launch HIP-event times and algorithmic
+    TFLOP/s against the bf16/fp16 MFMA peak (and, for the HBM-side encoder,
+    against min(MFMA, arithmetic intensity x HBM bandwidth))."""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd
+
+    cfg = W.PREFILL[name]
+    q, k, v = (t.to(dev) for t in W.prefill_inputs(cfg))
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.L), dtype=torch.float32, device=dev)
+    sc = float(np.float32(cfg.scale))
+    run = lambda: flash_attn_fwd(q, k, v, softmax_scale=sc, causal=cfg.causal, out=o, lse=lse)
+    between = None
+    if cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        between = lambda: flush.fill_(1)
+    settle(run)
+    st = ms_stats(time_launches(run, reps, between))
+    ms = st["mean"]
+    tf = cfg.flops() / (ms * 1e-3) / 1e12
+    ai = cfg.flops() / cfg.hbm_bytes()
+    roof = min(PEAK_MFMA_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
+    res = {"workload": f"{name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} L={cfg.L} D={cfg.D} "
+                       f"{str(cfg.dtype)[6:]} {'causal' if cfg.causal else 'bidirectional'}"
+                       + (" (cold: last-level cache flushed between launches)" if cold else ""),
+           "ms": st, "alg_flops_per_launch": cfg.flops(), "alg_bytes_per_launch": cfg.hbm_bytes(),
+           "value": round(tf, 3), "unit": "TFLOP/s",
+           "roofline": {"bound": "mfma" if roof >= PEAK_MFMA_BF16_TFLOPS else "hbm",
+                        "achieved": round(tf, 3), "peak": round(roof, 1), "unit": "TFLOP/s",
+                        "frac": round(tf / roof, 4),
+                        "frac_of_mfma_peak": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)},
+           "kernel": f"fwd_kernel<{str(cfg.dtype)[6:].replace('float16', 'f16')}, {cfg.D}, "
+                     f"{str(cfg.causal).lower()}>"}
+    if name == "tiny":
+        res["us"] = {k_: round(v_ * 1e3, 2) for k_, v_ in st.items() if k_ != "n"}
+    del q, k, v, o, lse
+    return res
+
+
+def _timed_block(run, reps):
+    settle(run)
+    return ms_stats(time_launches(run, reps))
+
+
+def time_paged(fmt, dev, reps=20):
     """The decode workload in a paged cache of 16-slot pages (native, int8
-    keys, or int8 keys and values): mean time of fa_decode_paged (split +
-    combine, HIP events on the launch stream) and algorithmic GB/s."""
+    keys, or int8 keys and values): time of fa_decode_paged (split + combine,
+    HIP events on the launch stream) and algorithmic GB/s."""
     import numpy as np
     import torch
 
@@ -261,26 +433,14 @@ def time_paged(fmt, dev, reps=10):
     run = lambda: flash_attn_decode_paged(q, kp, vp, table, lens_d, k_scales=ks, v_scales=vs,
                                           softmax_scale=sc, num_splits=cfg.num_splits,
                                           workspace=ws, out=o, lse=lse)
-    settle(run)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record()
-        run()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    mean = float(np.mean(ms))
+    st = _timed_block(run, reps)
     byts = W.paged_decode_bytes(cfg, lens, PAGE_SIZE, k_int8=k8, v_int8=v8)
-    gbs = byts / (mean * 1e-3) / 1e9
+    gbs = byts / (st["mean"] * 1e-3) / 1e9
     traffic = traffic_for(f"paged:{fmt}", source_digest(["fa_decode.hip", "fa_common.hpp"]))
     return {"workload": f"decode workload in {PAGE_SIZE}-slot pages, keys "
                         f"{'int8' if k8 else 'bf16'}, values {'int8' if v8 else 'bf16'}",
-            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
-                   "min": round(float(np.min(ms)), 5)},
-            "alg_bytes_per_step": byts, "value": round(gbs, 2), "unit": "GB/s",
-            "tokens_per_s": round(cfg.B / (mean * 1e-3), 1),
+            "ms": st, "alg_bytes_per_step": byts, "value": round(gbs, 2), "unit": "GB/s",
+            "tokens_per_s": round(cfg.B / (st["mean"] * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic}}
@@ -288,12 +448,13 @@ def time_paged(fmt, dev, reps=10):
 
 def time_bwd(dev, reps=10):
     """fa_bwd (prep + dQ + dK/dV kernels) on the Llama-2-7B-shaped causal
-    workload, fed by one untimed fa_fwd: mean time (HIP events on the launch
+    workload, fed by one untimed fa_fwd: time (HIP events on the launch
     stream) and algorithmic TFLOP/s (10*D per allowed pair per query head:
     the S, dP, dV, dQ and dK products)."""
     import numpy as np
     import torch
 
+    from exact_tiled_attention_fa_amd import _abi
     from exact_tiled_attention_fa_amd import workloads as W
     from exact_tiled_attention_fa_amd.attention import flash_attn_bwd, flash_attn_fwd
 
@@ -304,32 +465,19 @@ def time_bwd(dev, reps=10):
     sc = float(np.float32(cfg.scale))
     o, lse = flash_attn_fwd(q, k, v, softmax_scale=sc, causal=cfg.causal)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    from exact_tiled_attention_fa_amd import _abi
     ws = torch.empty((_abi.fa_bwd_workspace_size(cfg.B, cfg.Hq, cfg.L),), dtype=torch.uint8,
                      device=dev)
     run = lambda: flash_attn_bwd(q, k, v, o, lse, do, softmax_scale=sc, causal=cfg.causal, dq=dq,
                                  dk=dk, dv=dv, workspace=ws)
-    settle(run)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record()
-        run()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    mean = float(np.mean(ms))
+    st = _timed_block(run, reps)
     flops = cfg.flops() // 4 * 10
-    tf = flops / (mean * 1e-3) / 1e12
+    tf = flops / (st["mean"] * 1e-3) / 1e12
     # Q, O, dO read and dQ written (query side), K, V read and dK, dV written,
     # lse read: each once
     nq, nk = cfg.B * cfg.L * cfg.Hq * cfg.D * 2, cfg.B * cfg.L * cfg.Hkv * cfg.D * 2
     alg_bytes = 4 * nq + 4 * nk + cfg.B * cfg.Hq * cfg.L * 4
     return {"workload": "llama7b causal backward B=4 Hq=Hkv=32 L=4096 D=128 bf16 (dQ, dK, dV)",
-            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
-                   "min": round(float(np.min(ms)), 5)},
-            "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
+            "ms": st, "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
             "value": round(tf, 3), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
@@ -340,7 +488,7 @@ def time_bwd(dev, reps=10):
 def time_bwd_varlen(dev, reps=10):
     """fa_bwd_ex on the varlen16 workload (16 causal sequences packed back to
     back, lengths U[256, 4096], Hq=32, Hkv=8, D=128, bf16), fed by one untimed
-    packed forward: mean time (HIP events) and algorithmic TFLOP/s (10*D per
+    packed forward: time (HIP events) and algorithmic TFLOP/s (10*D per
     allowed pair per query head)."""
     import numpy as np
     import torch
@@ -364,31 +512,19 @@ def time_bwd_varlen(dev, reps=10):
     run = lambda: flash_attn_varlen_bwd(q, k, v, o, lse, do, cu, cu, L, L, softmax_scale=sc,
                                         causal=cfg.causal, window=cfg.window, dq=dq, dk=dk, dv=dv,
                                         workspace=ws)
-    settle(run)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record()
-        run()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    mean = float(np.mean(ms))
+    st = _timed_block(run, reps)
     flops = cfg.flops() // 4 * 10
-    tf = flops / (mean * 1e-3) / 1e12
+    tf = flops / (st["mean"] * 1e-3) / 1e12
     return {"workload": "varlen16 causal backward: 16 packed sequences U[256,4096], Hq=32 Hkv=8 "
                         "D=128 bf16 (dQ, dK, dV)",
-            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
-                   "min": round(float(np.min(ms)), 5)},
-            "alg_flops_per_launch": flops, "value": round(tf, 3), "unit": "TFLOP/s",
+            "ms": st, "alg_flops_per_launch": flops, "value": round(tf, 3), "unit": "TFLOP/s",
             "frac_mfma": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}
 
 
-def time_fp8(dev, reps=10):
+def time_fp8(dev, reps=20):
     """fa_fwd_fp8 on the Llama-2-7B-shaped causal workload with e4m3 Q, K, V:
-    mean time (HIP events on the launch stream) and algorithmic TFLOP/s
-    (4*D per allowed pair per query head) against the fp8 MFMA peak."""
+    time (HIP events on the launch stream) and algorithmic TFLOP/s (4*D per
+    allowed pair per query head) against the fp8 MFMA peak."""
     import numpy as np
     import torch
 
@@ -403,23 +539,12 @@ def time_fp8(dev, reps=10):
     sc = float(np.float32(cfg.scale))
     run = lambda: flash_attn_fwd_fp8(q8, k8, vt8, q_descale=ds, k_descale=ds, v_descale=ds,
                                      softmax_scale=sc, causal=True, out=o, lse=lse)
-    settle(run)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record()
-        run()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    mean = float(np.mean(ms))
-    tf = cfg.flops() / (mean * 1e-3) / 1e12
+    st = _timed_block(run, reps)
+    tf = cfg.flops() / (st["mean"] * 1e-3) / 1e12
     return {"workload": "llama7b causal prefill B=4 Hq=Hkv=32 L=4096 D=128, e4m3 Q/K/V "
                         "(per-tensor descale), bf16 O",
-            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
-                   "min": round(float(np.min(ms)), 5)},
-            "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3), "unit": "TFLOP/s",
+            "ms": st, "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3),
+            "unit": "TFLOP/s",
             # Q, K, V one byte per element read once, O (bf16) and lse written once
             "alg_bytes_per_launch": cfg.B * cfg.L * (3 * cfg.Hq * cfg.D + 2 * cfg.Hkv * cfg.D)
             + cfg.B * cfg.Hq * cfg.L * 4,
@@ -431,40 +556,30 @@ def time_fp8(dev, reps=10):
 
 
 def time_mfma_probe(q, dev, reps=10, iters=2048):
-    """The matrix cores' ceiling on the prefill's own data: the library's MFMA
-    probe (bf16 32x32x16 MFMAs only, in the forward step's chain pattern, two
-    waves per SIMD on every CU) timed with HIP events on the launch stream,
+    """The matrix cores' rate on the prefill's own data: the benchmark's MFMA
+    probe (libfa_probe.so: bf16 32x32x16 MFMAs only, in the forward step's
+    chain pattern, two waves per SIMD on every CU) timed with HIP events,
     once with its operands taken from the prefill's Q and once with every
     operand 1.0.  The MFMA rate depends on the operand values, so the first
     figure, not the published peak, is what the forward's MFMA work can reach
     on this data."""
-    import numpy as np
     import torch
 
-    from exact_tiled_attention_fa_amd.attention import mfma_probe
+    from exact_tiled_attention_fa_amd.probe import mfma_probe
 
     ones = torch.ones(1 << 24, dtype=torch.bfloat16, device=dev)
     res = {"about": "MFMA-only probe, bf16 32x32x16, 2 waves/SIMD, every CU; operands read "
                     "once from the given buffer"}
     for name, ops in (("prefill_q", q), ("constant_1", ones)):
         out, flops = mfma_probe(ops, iters)
-        settle(lambda: mfma_probe(ops, iters, out))
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        torch.cuda.synchronize()
-        for e0, e1 in evs:
-            e0.record()
-            mfma_probe(ops, iters, out)
-            e1.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-        res[name] = {"TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4)}
+        st = _timed_block(lambda: mfma_probe(ops, iters, out), reps)
+        res[name] = {"TFLOP/s": round(flops / (st["mean"] * 1e-3) / 1e12, 1), "ms": st}
     return res
 
 
-def time_masked(cfg, dev, reps=10):
-    """Mean launch time (ms, HIP events on the launch stream) of one
-    structured-mask workload, and its algorithmic TFLOP/s."""
+def time_masked(cfg, dev, reps=20):
+    """One structured-mask workload: launch times (HIP events on the launch
+    stream) and algorithmic TFLOP/s."""
     import numpy as np
     import torch
 
@@ -483,32 +598,24 @@ def time_masked(cfg, dev, reps=10):
         lse = torch.empty((cfg.nseq, cfg.Hq, lmax), dtype=torch.float32, device=dev)
         run = lambda: flash_attn_fwd(q, k, v, softmax_scale=sc, causal=cfg.causal,
                                      window=cfg.window, out=o, lse=lse)
-    settle(run)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record()
-        run()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    mean = float(np.mean(ms))
-    tf = cfg.flops() / (mean * 1e-3) / 1e12
+    st = _timed_block(run, reps)
+    tf = cfg.flops() / (st["mean"] * 1e-3) / 1e12
     lens = cfg.lengths()
     traffic = traffic_for(f"masks:{cfg.name}", source_digest(["fa_fwd.hip", "fa_common.hpp"]))
     return {"workload": f"{cfg.nseq} x L={'%d' % lens[0] if cfg.len_lo == cfg.len_hi else 'U[%d,%d]' % (cfg.len_lo, cfg.len_hi)}"
                         f" Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} {str(cfg.dtype)[6:]}"
                         f" causal={cfg.causal} window={tuple(cfg.window)}"
                         f" {'packed' if cfg.packed else 'dense'}",
-            "ms": {"mean": round(mean, 5), "median": round(float(np.median(ms)), 5),
-                   "min": round(float(np.min(ms)), 5)},
-            "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3), "unit": "TFLOP/s",
-            "alg_bytes_per_launch": cfg.hbm_bytes(),
+            "ms": st, "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3),
+            "unit": "TFLOP/s", "alg_bytes_per_launch": cfg.hbm_bytes(),
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
                          "traffic": traffic},
             "kernel": "fwd_kernel<bf16_t, 128, true>"}
+
+
+CONFIG_LEGS = [("gqa16k", 20, False), ("d256", 50, False), ("encoder", 50, True),
+               ("tiny", 1000, False)]
 
 
 def main():
@@ -545,34 +652,35 @@ def main():
     do_dec = args.only in (None, "decode")
     masks = {n: c for n, c in W.MASKED.items() if args.mask in (None, n)}
     paged_fmts = [f for f in PAGED_FORMATS if args.paged_format in (None, f)]
+
+    def finish(res):
+        if args.with_copy:
+            copy_calibration(args.with_copy, dev)
+        res["lib"] = info
+        print(json.dumps(res), flush=True)
+
+    if args.only == "config":
+        legs = {n: (r, c) for n, r, c in CONFIG_LEGS}
+        legs["llama7b"] = (50, False)
+        if args.config not in legs:
+            sys.exit(f"--only config needs --config in {sorted(legs)}")
+        reps, cold = legs[args.config]
+        print(f"# prefill workload {args.config}", file=sys.stderr, flush=True)
+        return finish({"configs": {args.config: time_prefill_cfg(
+            args.config, dev, args.reps or reps, cold)}})
     if args.only == "fp8":
         print("# fp8 forward workload", file=sys.stderr, flush=True)
-        res = time_fp8(dev)
-        if args.with_copy:
-            copy_calibration(args.with_copy, dev)
-        print(json.dumps({"fp8": res, "lib": info}), flush=True)
-        return
+        return finish({"fp8": time_fp8(dev, args.reps or 20)})
     if args.only == "bwd":
         print("# backward workload", file=sys.stderr, flush=True)
-        res = time_bwd(dev)
-        if args.with_copy:
-            copy_calibration(args.with_copy, dev)
-        print(json.dumps({"backward": res, "lib": info}), flush=True)
-        return
+        return finish({"backward": time_bwd(dev, args.reps or 10)})
     if args.only == "paged":
         print("# paged decode workloads", file=sys.stderr, flush=True)
-        res = {f: time_paged(f, dev) for f in paged_fmts}
-        if args.with_copy:
-            copy_calibration(args.with_copy, dev)
-        print(json.dumps({"paged": res, "lib": info}), flush=True)
-        return
+        return finish({"paged": {f: time_paged(f, dev, args.reps or 20) for f in paged_fmts}})
     if args.only == "masks":
         print("# structured-mask workloads", file=sys.stderr, flush=True)
-        res = {n: time_masked(c, dev) for n, c in masks.items()}
-        if args.with_copy:
-            copy_calibration(args.with_copy, dev)
-        print(json.dumps({"masks": res, "lib": info}), flush=True)
-        return
+        return finish({"masks": {n: time_masked(c, dev, args.reps or 20)
+                                 for n, c in masks.items()}})
 
     pcfg = W.PREFILL["llama7b"]
     dcfg = W.DECODE["decode"]
@@ -605,6 +713,8 @@ def main():
         if evs is not None:
             evs[2].record()
 
+    print(f"# settle {args.settle} s", file=sys.stderr, flush=True)
+    settle_steps = settle(step, args.settle) if args.settle > 0 else 0
     print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -619,9 +729,10 @@ def main():
     wall = time.perf_counter() - t0
     pf_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-
-    if args.with_copy:
-        copy_calibration(args.with_copy, dev)
+    sclk = None
+    if not args.no_sclk:
+        print("# graphics clock under the step's load (amd-smi)", file=sys.stderr, flush=True)
+        sclk = sclk_under_load(step)
 
     out = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
@@ -634,27 +745,26 @@ def main():
                                   "D": pcfg.D, "causal": True},
                       "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "D": dcfg.D,
                                  "num_splits": dcfg.num_splits},
-                      "lib": info}}
+                      "lib": info},
+           "settle_s": args.settle, "settle_steps": settle_steps, "sclk": sclk}
     if do_pf:
-        ms = float(np.mean(pf_ms))
-        tf = pcfg.flops() / (ms * 1e-3) / 1e12
+        st = ms_stats(pf_ms)
+        tf = pcfg.flops() / (st["mean"] * 1e-3) / 1e12
         out["value"] = round(tf, 3)
-        out["prefill_ms"] = {"mean": round(ms, 5), "median": round(float(np.median(pf_ms)), 5),
-                             "min": round(float(np.min(pf_ms)), 5)}
+        out["prefill_ms"] = st
         out["roofline"] = {"bound": "mfma", "achieved": round(tf, 3),
                            "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
                            "traffic": traffic_for("fwd_kernel", source_digest(
                                ["fa_fwd.hip", "fa_common.hpp"])),
                            "kernel": "fwd_kernel<bf16_t, 128, true>",
-                           "alg_flops_per_launch": pcfg.flops()}
+                           "alg_flops_per_launch": pcfg.flops(),
+                           "alg_bytes_per_launch": pcfg.hbm_bytes()}
     if do_dec:
-        dms = float(np.mean(dec_ms))
+        st = ms_stats(dec_ms)
         byts = W.decode_bytes(dcfg, lens_c)
-        gbs = byts / (dms * 1e-3) / 1e9
-        out["decode"] = {"value": round(gbs, 2), "unit": "GB/s",
-                         "ms": {"mean": round(dms, 5), "median": round(float(np.median(dec_ms)), 5),
-                                "min": round(float(np.min(dec_ms)), 5)},
+        gbs = byts / (st["mean"] * 1e-3) / 1e9
+        out["decode"] = {"value": round(gbs, 2), "unit": "GB/s", "ms": st,
                          "alg_bytes_per_step": byts,
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 2),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -663,6 +773,11 @@ def main():
                                           ["fa_decode.hip", "fa_common.hpp"]))}}
         if out["value"] is None:
             out["value"], out["unit"] = round(gbs, 2), "GB/s"
+    if do_pf and not args.no_configs:
+        out["configs"] = {}
+        for name, reps, cold in CONFIG_LEGS:
+            print(f"# prefill workload {name}", file=sys.stderr, flush=True)
+            out["configs"][name] = time_prefill_cfg(name, dev, reps, cold)
     if do_dec and not args.no_paged:
         print("# paged decode workloads", file=sys.stderr, flush=True)
         out["decode"]["paged"] = {f: time_paged(f, dev) for f in paged_fmts}
@@ -676,11 +791,13 @@ def main():
     if do_pf and not args.no_masks:
         print("# structured-mask workloads", file=sys.stderr, flush=True)
         out["masks"] = {name: time_masked(cfg, dev) for name, cfg in masks.items()}
-    if do_pf and not args.no_probe:
-        print("# matrix-core ceiling probe", file=sys.stderr, flush=True)
+    if do_pf and args.probe:
+        print("# matrix-core probe", file=sys.stderr, flush=True)
         out["mfma_probe"] = time_mfma_probe(q, dev)
-        out["mfma_probe"]["prefill_frac_of_prefill_q_ceiling"] = round(
+        out["mfma_probe"]["prefill_frac_of_prefill_q_rate"] = round(
             out["value"] / out["mfma_probe"]["prefill_q"]["TFLOP/s"], 4)
+    if args.with_copy:
+        copy_calibration(args.with_copy, dev)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         if do_pf:
@@ -689,25 +806,6 @@ def main():
             out.setdefault("decode", {})["cpu_baseline"] = cpu_baseline_decode(
                 dcfg, dq_c, kc_c, vc_c, lens_c, dscale)
     print(json.dumps(out), flush=True)
-
-    if args.all_configs:
-        for name, cfg in W.PREFILL.items():
-            qq, kk, vv = (t.to(dev) for t in W.prefill_inputs(cfg))
-            sc = float(np.float32(cfg.scale))
-            settle(lambda: flash_attn_fwd(qq, kk, vv, softmax_scale=sc, causal=cfg.causal))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 20
-            e0.record()
-            for _ in range(reps):
-                flash_attn_fwd(qq, kk, vv, softmax_scale=sc, causal=cfg.causal)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            tf = cfg.flops() / (ms * 1e-3) / 1e12
-            print(json.dumps({"workload": name, "ms": round(ms, 5), "TFLOP/s": round(tf, 2),
-                              "frac_mfma": round(tf / PEAK_MFMA_BF16_TFLOPS, 4),
-                              "GB/s": round(cfg.hbm_bytes() / (ms * 1e-3) / 1e9, 1)}), flush=True)
-            del qq, kk, vv
 
 
 if __name__ == "__main__":

@@ -53,8 +53,6 @@ SIGNATURES = {
                        _F, _I, _I, _I, _P, _Z, _I, _P]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_info": (ctypes.c_char_p, []),
-    "fa_probe_mfma_out_len": (_Z, []),
-    "fa_probe_mfma_bf16": (_I, [_P, _Z, _P, _Z, _I, ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -156,14 +154,3 @@ def fa_last_error() -> str:
 
 def fa_info() -> str:
     return (load().fa_info() or b"").decode()
-
-
-def fa_probe_mfma_out_len() -> int:
-    return load().fa_probe_mfma_out_len()
-
-
-def fa_probe_mfma_bf16(operands, operand_bytes, out, out_len, iters, flops_per_launch,
-                       stream) -> int:
-    """flops_per_launch: a ctypes.c_double, filled on success."""
-    return load().fa_probe_mfma_bf16(operands, operand_bytes, out, out_len, iters,
-                                     ctypes.byref(flops_per_launch), stream)

@@ -385,31 +385,3 @@ def flash_attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: tor
     if st != _abi.FA_OK:
         raise FAError(st, "fa_decode_paged")
     return out, lse
-
-
-def mfma_probe(operands: torch.Tensor, iters: int, out=None):
-    """Measurement helper, not attention: one launch of the matrix-core probe
-    (bf16 32x32x16 MFMAs in the forward step's chain pattern) on the bytes of
-    ``operands`` (any contiguous GPU tensor, read as bf16, size a multiple of
-    16 bytes).  Returns (out, flops): each thread's accumulator sum (float32,
-    exactly 4096 * iters when every operand is 1.0) and the flops the launch
-    executes.  Timing it on a workload's own data gives the MFMA ceiling for
-    that data."""
-    import ctypes
-
-    _check_dev(operands, "operands")
-    n = _abi.fa_probe_mfma_out_len()
-    if n == 0:
-        raise FAError(_abi.FA_ERR_HIP, "fa_probe_mfma_out_len")
-    if out is None:
-        out = torch.empty(n, dtype=torch.float32, device=operands.device)
-    _check_dev(out, "out")
-    if out.dtype != torch.float32:
-        raise ValueError("out must be float32")
-    flops = ctypes.c_double(0.0)
-    st = _abi.fa_probe_mfma_bf16(operands.data_ptr(), operands.numel() * operands.element_size(),
-                                 out.data_ptr(), out.numel(), int(iters), flops,
-                                 _stream_handle(operands.device))
-    if st != _abi.FA_OK:
-        raise FAError(st, "fa_probe_mfma_bf16")
-    return out, flops.value

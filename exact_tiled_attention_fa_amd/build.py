@@ -1,4 +1,6 @@
-"""Build libfa.so (gfx950) in-tree with hipcc.
+"""Build libfa.so (gfx950) in-tree with hipcc, and the benchmark's
+matrix-core probe as a library of its own (libfa_probe.so, not part of the
+attention ABI).
 
     python -m exact_tiled_attention_fa_amd.build [-v]
 
@@ -25,8 +27,9 @@ OUT_DIR = PKG / "_lib"
 LIB = OUT_DIR / "libfa.so"
 OBJ_DIR = ROOT / "_build"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip",
-           "fa_probe.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
+PROBE_SOURCE = "probe/mfma_probe.hip"
+PROBE_LIB = OUT_DIR / "libfa_probe.so"
 ARCH = "gfx950"
 
 
@@ -64,23 +67,31 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print("\n".join(lines))
 
 
+def _obj(src: str) -> Path:
+    return OBJ_DIR / (src.replace("/", "_").replace(".", "_") + ".o")
+
+
+def _link(objs, lib: Path, verbose: bool) -> None:
+    tmp = lib.with_suffix(".so.tmp")
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)],
+         verbose)
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False) -> Path:
-    """Compile every source and link libfa.so; always rebuilds."""
+    """Compile every source and link libfa.so and libfa_probe.so; always
+    rebuilds.  Returns the path of libfa.so."""
     OUT_DIR.mkdir(parents=True, exist_ok=True)
     OBJ_DIR.mkdir(parents=True, exist_ok=True)
     cc = hipcc()
-    objs = []
     cmds = []
-    for src in SOURCES:
-        obj = OBJ_DIR / (src.replace(".", "_") + ".o")
-        objs.append(obj)
+    for src in SOURCES + [PROBE_SOURCE]:
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([cc, *common_flags(), *lang, "-c", str(CSRC / src), "-o", str(obj)])
+        cmds.append([cc, *common_flags(), *lang, "-c", str(CSRC / src), "-o", str(_obj(src))])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = OUT_DIR / "libfa.so.tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)], verbose)
-    os.replace(tmp, LIB)
+    _link([_obj(s) for s in SOURCES], LIB, verbose)
+    _link([_obj(PROBE_SOURCE)], PROBE_LIB, verbose)
     return LIB
 
 

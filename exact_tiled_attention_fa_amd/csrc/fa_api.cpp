@@ -390,42 +390,6 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                    stream);
 }
 
-namespace {
-// Two workgroups of the probe per compute unit of the current device; 0 if the
-// device cannot be queried.
-int probe_blocks() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return 2 * cus;
-}
-}  // namespace
-
-size_t fa_probe_mfma_out_len(void) { return (size_t)fa::mfma_probe_threads(probe_blocks()); }
-
-fa_status fa_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* out,
-                             size_t out_len, int iters, double* flops_per_launch,
-                             hipStream_t stream) {
-  FA_TRY(check_ptr(operands, "operands"));
-  FA_TRY(check_ptr(out, "out"));
-  if (!flops_per_launch) return fail(FA_ERR_INVALID_ARGUMENT, "flops_per_launch is NULL");
-  if (operand_bytes < 16 || operand_bytes % 16)
-    return fail(FA_ERR_INVALID_ARGUMENT, "operand_bytes=%zu must be a positive multiple of 16",
-                operand_bytes);
-  if (iters < 1 || iters > (1 << 20))
-    return fail(FA_ERR_INVALID_ARGUMENT, "iters=%d must be in [1, 2^20]", iters);
-  const int nblocks = probe_blocks();
-  if (nblocks < 1) return fail(FA_ERR_HIP, "cannot query the current device's compute units");
-  const size_t need = (size_t)fa::mfma_probe_threads(nblocks);
-  if (out_len < need)
-    return fail(FA_ERR_INVALID_ARGUMENT, "out holds %zu floats; the probe writes %zu", out_len, need);
-  hipError_t e = fa::launch_mfma_probe(operands, (long)(operand_bytes / 16), out, nblocks, iters,
-                                       stream);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
-  *flops_per_launch = fa::mfma_probe_flops(nblocks, iters);
-  return ok();
-}
-
 const char* fa_last_error(void) { return g_err; }
 
 const char* fa_info(void) {

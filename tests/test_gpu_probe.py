@@ -1,13 +1,14 @@
-"""The matrix-core ceiling probe (a measurement helper used by the benchmark):
-it executes the MFMAs it counts, on the operands it is given."""
+"""The matrix-core ceiling probe (the benchmark's measurement helper, in its own
+library libfa_probe.so): it executes the MFMAs it counts, on the operands it
+is given."""
 
 from __future__ import annotations
 
 import pytest
 import torch
 
-from exact_tiled_attention_fa_amd import _abi
-from exact_tiled_attention_fa_amd.attention import FAError, mfma_probe
+from exact_tiled_attention_fa_amd import probe
+from exact_tiled_attention_fa_amd.probe import mfma_probe
 from gpu_util import say
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +23,7 @@ def test_probe_constant_operands_closed_form(iters, gpu):
     ones = torch.ones(4096, dtype=torch.bfloat16, device=gpu)
     out, flops = mfma_probe(ones, iters)
     torch.cuda.synchronize()
-    n = _abi.fa_probe_mfma_out_len()
+    n = probe.out_len()
     assert out.numel() == n and n % 256 == 0
     assert torch.all(out == 4096.0 * iters)
     assert flops == (n // 64) * iters * 16 * 2 * 32 * 32 * 16
@@ -44,6 +45,6 @@ def test_probe_reads_the_given_operands(gpu):
 
 def test_probe_rejects_short_output(gpu):
     ones = torch.ones(64, dtype=torch.bfloat16, device=gpu)
-    out = torch.empty(_abi.fa_probe_mfma_out_len() - 1, dtype=torch.float32, device=gpu)
-    with pytest.raises(FAError):
+    out = torch.empty(probe.out_len() - 1, dtype=torch.float32, device=gpu)
+    with pytest.raises(RuntimeError):
         mfma_probe(ones, 1, out)
