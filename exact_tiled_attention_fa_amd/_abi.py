@@ -44,6 +44,7 @@ SIGNATURES = {
                            _F, _F, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
+    "fa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                              _I, _I, _I, _P, _Z, _I, _P]),
     "fa_bwd_workspace_size": (_Z, [_I, _I, _I]),
@@ -119,6 +120,12 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale
               workspace, workspace_bytes, dtype, stream) -> int:
     return load().fa_decode(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale,
                             num_splits, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale,
+                      num_splits, dtype, stream) -> int:
+    return load().fa_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D,
+                                    scale, num_splits, dtype, stream)
 
 
 def fa_decode_paged(q, k_pages, v_pages, k_scales, v_scales, block_table, seqlens, o, lse, B, Hq,

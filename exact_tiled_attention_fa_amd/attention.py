@@ -298,9 +298,12 @@ def decode_workspace(B: int, Hq: int, D: int, num_splits: int, device) -> torch.
 
 def flash_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       seqlens: torch.Tensor, *, softmax_scale=None, num_splits: int = 8,
-                      workspace=None, out=None, lse=None):
+                      workspace=None, out=None, lse=None, noalloc: bool = False):
     """One query token per sequence.  q [B,Hq,D]; caches [B,Lk_max,Hkv,D];
     seqlens int32 [B] on the device.  Returns (o [B,Hq,D], lse [B,Hq] float32).
+    With ``noalloc`` the call goes to fa_decode_noalloc, whose split partials
+    live in the library's fixed device array (no workspace; with ``out`` and
+    ``lse`` given, nothing is allocated at all).
     """
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens, "seqlens")):
         _check_dev(t, n)
@@ -315,12 +318,22 @@ def flash_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if k_cache.shape[0] != B or Dk != D:
         raise ValueError("batch or head_dim mismatch between q and the caches")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    if workspace is None:
-        workspace = decode_workspace(B, Hq, D, num_splits, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        st = _abi.fa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                                    Lk_max, D, scale, num_splits, _DTYPES[q.dtype],
+                                    _stream_handle(q.device))
+        if st != _abi.FA_OK:
+            raise FAError(st, "fa_decode_noalloc")
+        return out, lse
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, D, num_splits, q.device)
     st = _abi.fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
                         out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Lk_max, D, scale, num_splits,
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -27,7 +27,8 @@ OUT_DIR = PKG / "_lib"
 LIB = OUT_DIR / "libfa.so"
 OBJ_DIR = ROOT / "_build"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_decode_noalloc.hip", "fa_bwd.hip",
+           "fa_fwd_fp8.hip"]
 PROBE_SOURCE = "probe/mfma_probe.hip"
 PROBE_LIB = OUT_DIR / "libfa_probe.so"
 ARCH = "gfx950"

@@ -196,10 +196,22 @@ size_t fa_decode_workspace_size(int B, int Hq, int D, int num_splits) {
   return fa::decode_workspace_bytes(B, Hq, D, num_splits);
 }
 
-fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
-                    void* o, float* lse, int B, int Hq, int Hkv, int Lk_max, int D, float scale,
-                    int num_splits, void* workspace, size_t workspace_bytes, fa_dtype dtype,
-                    hipStream_t stream) {
+}  // extern "C"
+
+namespace fa {
+
+fa_status set_error(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fa_status check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                            const int* seqlens, const void* o, const float* lse, int B, int Hq,
+                            int Hkv, int Lk_max, int D, float scale, int num_splits,
+                            fa_dtype dtype) {
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(k_cache, "k_cache"));
   FA_TRY(check_ptr(v_cache, "v_cache"));
@@ -208,7 +220,6 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
     return fail(FA_ERR_INVALID_ARGUMENT, "seqlens is not 4-byte aligned");
   FA_TRY(check_ptr(o, "o"));
   FA_TRY(check_ptr(lse, "lse"));
-  FA_TRY(check_ptr(workspace, "workspace"));
   if (B < 1 || Hq < 1 || Hkv < 1 || Lk_max < 1 || D < 1)
     return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Lk_max=%d D=%d)",
                 B, Hq, Hkv, Lk_max, D);
@@ -225,6 +236,20 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
     return fail(FA_ERR_INVALID_ARGUMENT, "B*Lk_max*Hkv exceeds 2^31-1 rows");
   if ((long long)Hkv * ((Hq / Hkv + 15) / 16) > 65535 || B > 65535)
     return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (B or Hq exceeds 65535)");
+  return FA_OK;
+}
+
+}  // namespace fa
+
+extern "C" {
+
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                    void* o, float* lse, int B, int Hq, int Hkv, int Lk_max, int D, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                    hipStream_t stream) {
+  FA_TRY(fa::check_decode_args(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lk_max, D, scale,
+                               num_splits, dtype));
+  FA_TRY(check_ptr(workspace, "workspace"));
   const size_t need = fa::decode_workspace_bytes(B, Hq, D, num_splits);
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, needs %zu", workspace_bytes,

@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa.h"
 #include "fa_sched.hpp"
 
 namespace fa {
@@ -85,6 +86,16 @@ struct Fp8Args {
   const int* cu_k = nullptr;
   int total_q = 0, total_k = 0;
 };
+
+// Host-side pieces of the C ABI shared by its source files (fa_api.cpp):
+// set_error records the calling thread's fa_last_error() text and returns st;
+// check_decode_args validates fa_decode's arguments other than the workspace
+// (FA_OK, or the status with the text recorded), before any HIP call.
+fa_status set_error(fa_status st, const char* fmt, ...);
+fa_status check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                            const int* seqlens, const void* o, const float* lse, int B, int Hq,
+                            int Hkv, int Lk_max, int D, float scale, int num_splits,
+                            fa_dtype dtype);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);

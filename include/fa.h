@@ -208,6 +208,26 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
                     fa_dtype dtype, hipStream_t stream);
 
 /*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, kernels and results as fa_decode, minus
+ * the workspace: the split partials live in a fixed 32 MiB array in device
+ * memory that the library holds on each GPU it runs on until the process
+ * ends.  Limit: B * Hq * num_splits * (D + 1) * 4 bytes must fit in 32 MiB
+ * (65,027 (head, split) pairs at D = 128); larger calls return
+ * FA_ERR_INVALID_ARGUMENT before any device call.  The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress); no
+ * call allocates or frees memory.  Every call on one GPU uses the same array:
+ * calls that overlap on one GPU (different streams or host threads without
+ * ordering between them) race and give wrong results; calls ordered on one
+ * stream are safe.
+ */
+fa_status fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv,
+                            int Lk_max, int D, float scale, int num_splits, fa_dtype dtype,
+                            hipStream_t stream);
+
+/*
  * fa_decode_paged -- fa_decode over a paged KV cache whose keys, or keys and
  * values, may be stored as int8.
  *

@@ -38,7 +38,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_fp8_ex", "fa_bwd", "fa_bwd_ex",
          "fa_bwd_workspace_size",
-         "fa_decode",
+         "fa_decode", "fa_decode_noalloc",
          "fa_decode_paged", "fa_decode_workspace_size", "fa_last_error", "fa_info"])
 
 
@@ -359,3 +359,22 @@ def test_probe_library_rejects():
                                      a["iters"], ctypes.byref(fl), None)
         assert st == 1, kw
     assert fl.value == 0.0
+
+
+def test_decode_noalloc_rejects_before_the_device(lib):
+    """fa_decode_noalloc validates like fa_decode and rejects calls whose split
+    partials exceed its 32 MiB static array, all before any device call."""
+    def call(**kw):
+        a = dict(q=A16, k=A16, v=A16, seqlens=A16, o=A16, lse=A16, B=4, Hq=8, Hkv=2, Lk_max=64,
+                 D=128, scale=0.1, splits=8, dtype=_abi.FA_BF16)
+        a.update(kw)
+        return _abi.fa_decode_noalloc(a["q"], a["k"], a["v"], a["seqlens"], a["o"], a["lse"],
+                                      a["B"], a["Hq"], a["Hkv"], a["Lk_max"], a["D"], a["scale"],
+                                      a["splits"], a["dtype"], None)
+
+    assert call(q=None) == _abi.FA_ERR_INVALID_ARGUMENT
+    assert call(splits=0) == _abi.FA_ERR_INVALID_ARGUMENT
+    assert call(D=96) == _abi.FA_ERR_UNSUPPORTED
+    # 256 sequences x 64 heads x 8 splits x 129 floats = 67.6 MB > 32 MiB
+    st = call(B=256, Hq=64, Hkv=8)
+    assert st == _abi.FA_ERR_INVALID_ARGUMENT and "static scratch" in _abi.fa_last_error()
