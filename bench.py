@@ -80,6 +80,9 @@ def parse():
                    help="also time the matrix-core probe (libfa_probe.so) on the prefill's Q "
                         "and on constant operands")
     p.add_argument("--no-sclk", action="store_true", help="do not read the clock from amd-smi")
+    p.add_argument("--rates", action="store_true",
+                   help="only run the instruction-rate probes (libfa_probe.so): SIMD cycles of "
+                        "MFMA, FMA and exp mixes at 1 and 2 waves per SIMD")
     p.add_argument("--paged-format", choices=["native", "k8", "kv8"], default=None,
                    help="time only this paged-cache format")
     p.add_argument("--no-paged", action="store_true",
@@ -90,6 +93,15 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs of this script with "
                         "--with-copy (FETCH_SIZE, then WRITE_SIZE) into profiles/traffic.json")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                   help="no GPU work: from a rocprofv3 --kernel-trace --stats run of the default "
+                        "bench and the JSON line it printed, print the per-kernel statistics and "
+                        "the step prefill's average over the timed steps")
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                   help="no GPU work: per-dispatch medians of every counter in rocprofv3 --pmc "
+                        "runs, for the kernels named by --kernel-match")
+    p.add_argument("--kernel-match", default="fwd_kernel<fa::bf16_t, 128, true>",
+                   help="substring of the kernel name for --summarize-counters")
     p.add_argument("--pmc-key", default=None,
                    help="with --summarize-pmc on a run of --only masks --mask NAME: record the "
                         "forward kernel's traffic under this key (e.g. masks:NAME)")
@@ -182,6 +194,65 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_mib: int, key=None) -> di
                          "fetch_kib": sum(a for a, _ in parts), "write_kib": sum(b for _, b in parts),
                          "bytes_per_launch": int(sum(a * ff + b * fw for a, b in parts) * 1024)}
     return out
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_trace(trace_dir: str, bench_json: str) -> dict:
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run of the
+    default bench, and the average duration of the step's prefill launches
+    over the timed steps only (the dispatches after the settle and warm-up
+    steps the bench's JSON line reports), to set against its HIP-event
+    figure."""
+    import statistics
+
+    with open(bench_json) as f:
+        line = [ln for ln in f.read().splitlines() if ln.startswith("{")][-1]
+    b = json.loads(line)
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    fwd = [r for r in trace if "fwd_kernel<fa::bf16_t, 128, true>" in r["Kernel_Name"]]
+    first = b["settle_steps"] + b["warmup"]
+    timed = fwd[first:first + b["steps"]]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+    out = {"bench_prefill_ms_mean": b["prefill_ms"]["mean"], "bench_value": b["value"],
+           "bench_frac": b["roofline"]["frac"],
+           "trace_timed_prefill_us_mean": round(statistics.mean(dur), 2) if dur else None,
+           "trace_timed_prefill_us_median": round(statistics.median(dur), 2) if dur else None,
+           "timed_dispatches": len(dur), "first_timed_dispatch": first,
+           "stats": [{k: r[k] for k in ("Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage")
+                      if k in r} for r in stats]}
+    if dur:
+        tf = b["roofline"]["alg_flops_per_launch"] / (statistics.mean(dur) * 1e-6) / 1e12
+        out["trace_timed_prefill_tflops"] = round(tf, 1)
+        out["trace_timed_prefill_frac"] = round(tf / PEAK_MFMA_BF16_TFLOPS, 4)
+    return out
+
+
+def summarize_counters(dirs, match: str) -> dict:
+    """Median over dispatches of each counter of the kernels whose name holds
+    ``match``, from one or more rocprofv3 --pmc runs (one pass each)."""
+    import statistics
+
+    vals = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if match in r["Kernel_Name"]:
+                key = (d, r["Dispatch_Id"])  # dispatch ids restart in every run
+                vals.setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+                vals[r["Counter_Name"]][key] += float(r["Counter_Value"])
+    return {k: {"median": statistics.median(v.values()), "dispatches": len(v)}
+            for k, v in sorted(vals.items())}
 
 
 def cpu_baseline_prefill(cfg, q, k, v, scale, target_s):
@@ -634,6 +705,12 @@ def main():
             json.dump(merged, f, indent=1)
         print(json.dumps(t))
         return
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(*args.summarize_trace), indent=1))
+        return
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters, args.kernel_match), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.exit("bench.py measures one GPU only: the library has no multi-GPU path "
                  "(run with --gpus 1).")
@@ -648,6 +725,21 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     info = _abi.fa_info()
+    if args.rates:
+        from exact_tiled_attention_fa_amd import probe
+
+        g = torch.Generator().manual_seed(5)
+        ops = torch.randn((1 << 22,), generator=g).to(torch.bfloat16).to(dev)
+        ones = torch.ones((1 << 22,), dtype=torch.bfloat16, device=dev)
+        res = {}
+        for data, t in (("random_bf16", ops), ("constant_1", ones)):
+            for n in (1, 2):
+                for vg in (False, True):
+                    key = f"{data}/{n}_waves_per_simd/{'archvgpr' if vg else 'accvgpr'}_acc"
+                    print(f"# rates: {key}", file=sys.stderr, flush=True)
+                    res[key] = probe.rates(t, n, vgpr_acc=vg)
+        print(json.dumps({"rates": res, "lib": info}), flush=True)
+        return
     do_pf = args.only in (None, "prefill")
     do_dec = args.only in (None, "decode")
     masks = {n: c for n, c in W.MASKED.items() if args.mask in (None, n)}

@@ -29,7 +29,9 @@ OBJ_DIR = ROOT / "_build"
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_decode_noalloc.hip", "fa_bwd.hip",
            "fa_fwd_fp8.hip"]
-PROBE_SOURCE = "probe/mfma_probe.hip"
+PROBE_SOURCES = ["probe/mfma_probe.hip", "probe/rate_probe.hip", "probe/rate_probe_vgpr.hip"]
+# per-source extra flags
+EXTRA_FLAGS = {"probe/rate_probe_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 PROBE_LIB = OUT_DIR / "libfa_probe.so"
 ARCH = "gfx950"
 
@@ -86,13 +88,14 @@ def build(verbose: bool = False) -> Path:
     OBJ_DIR.mkdir(parents=True, exist_ok=True)
     cc = hipcc()
     cmds = []
-    for src in SOURCES + [PROBE_SOURCE]:
+    for src in SOURCES + PROBE_SOURCES:
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([cc, *common_flags(), *lang, "-c", str(CSRC / src), "-o", str(_obj(src))])
+        cmds.append([cc, *common_flags(), *EXTRA_FLAGS.get(src, []), *lang, "-c", str(CSRC / src),
+                     "-o", str(_obj(src))])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     _link([_obj(s) for s in SOURCES], LIB, verbose)
-    _link([_obj(PROBE_SOURCE)], PROBE_LIB, verbose)
+    _link([_obj(s) for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 
