@@ -765,7 +765,9 @@ def main():
         return finish({"fp8": time_fp8(dev, args.reps or 20)})
     if args.only == "bwd":
         print("# backward workload", file=sys.stderr, flush=True)
-        return finish({"backward": time_bwd(dev, args.reps or 10)})
+        res = time_bwd(dev, args.reps or 10)
+        res["varlen16"] = time_bwd_varlen(dev, args.reps or 10)
+        return finish({"backward": res})
     if args.only == "paged":
         print("# paged decode workloads", file=sys.stderr, flush=True)
         return finish({"paged": {f: time_paged(f, dev, args.reps or 20) for f in paged_fmts}})

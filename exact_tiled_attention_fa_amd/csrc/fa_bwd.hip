@@ -73,6 +73,7 @@ struct BwdParams {
   float scale2;  // |scale| * log2(e), >= 1e-30
   float scale;   // signed scale (factor of dQ and dK)
   uint32_t qxor; // sign flip of q for negative scales
+  int xcd_wq, xcd_wk;  // work-list windows of the dq and dkdv grids (xcd_work_item)
 };
 
 // XOR on a row's 16-byte chunk index in the LDS tiles (row reads of 16
@@ -274,7 +275,7 @@ void bwd_dq_kernel(const BwdParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int nqt = (p.Lq + kBM - 1) / kBM;
   int b, h, tt;
-  bwd_item((int)blockIdx.x, p.B, Hq, b, h, tt);
+  xcd_work_item((int)blockIdx.x, p.B, Hq, nqt, p.xcd_wq, b, h, tt);
   const int qt = CAUSAL ? nqt - 1 - tt : tt;  // heaviest (last, under a causal mask) first
   const SeqRows sr = seq_rows(p, b);
   const int Lq = sr.Lq, Lk = sr.Lk;
@@ -498,7 +499,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const bool sw = ((wu & 1) ^ ((wu >> 2) & 1)) != 0;
   // Key tiles ascending: under a causal mask the first see the most queries.
   int b, kvh, kt;
-  bwd_item((int)blockIdx.x, p.B, Hkv, b, kvh, kt);
+  xcd_work_item((int)blockIdx.x, p.B, Hkv, (p.Lk + KBM - 1) / KBM, p.xcd_wk, b, kvh, kt);
   const SeqRows sr = seq_rows(p, b);
   const int Lq = sr.Lq, Lk = sr.Lk;
   const int k0 = kt * KBM;
@@ -739,9 +740,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gq((unsigned)((long)((a.Lq + kBM - 1) / kBM) * a.Hq * a.B));
+  const int nqt = (a.Lq + kBM - 1) / kBM;
+  const dim3 gq((unsigned)((long)nqt * a.Hq * a.B));
   constexpr int NW = KvWaves<D>::value, KBM = NW / 2 * kBR;
-  const dim3 gk((unsigned)((long)((a.Lk + KBM - 1) / KBM) * a.Hkv * a.B));
+  const int nkt = (a.Lk + KBM - 1) / KBM;
+  const dim3 gk((unsigned)((long)nkt * a.Hkv * a.B));
+  // Block order: each XCD walks windows of a few (sequence, head) rows with
+  // the heaviest tiles first (xcd_work_item), so the K/V (dq) or Q/dO (dkdv)
+  // streams that run at once on an XCD belong to few heads and stay in its
+  // L2.  Workgroups resident per CU: dq 2 (1 at D = 256), dkdv 1.
+  p.xcd_wq = xcd_window(a.B, a.Hq, a.Hkv, nqt, D <= 128 ? 2 : 1);
+  p.xcd_wk = xcd_window(a.B, a.Hkv, a.Hkv, nkt, 1);
   if (a.causal) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), gq, dim3(kBT), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -41,18 +41,20 @@ inline int xcd_window(int B, int Hq, int Hkv, int nqt, int blocks_per_cu) {
   return rows;
 }
 
-// Block -> (sequence b, query head h, query-tile rank) for the forward
-// kernels, over a grid of nqt * B * Hq blocks.  Blocks are dealt to the 8
+// Block -> (sequence b, head h, tile rank) over a grid of nqt * B * Hq
+// blocks: the forward kernels' (query head, query tile), the backward dq
+// kernel's (query head, query tile) and its dkdv kernel's (K/V head, key
+// tile).  Blocks are dealt to the 8
 // XCDs round-robin and start in index order.  When Hq is a multiple of 8,
 // XCD x takes query heads [x*Hq/8, (x+1)*Hq/8) of every sequence, which
 // balances the XCDs even when packed sequences differ in length.  Its rows
 // (sequence, head) are walked in windows of W adjacent rows, rank-major
 // within a window (rank 0 of each row, then rank 1, ...): the heavy ranks of
 // every window start together and the grid ends on light blocks, while the
-// few rows of a window keep their K/V tiles in L2.  W (from xcd_window) is a
-// multiple of gcd(Hq/Hkv, Hq/8), so the heads reading one K/V head run side
-// by side.  Otherwise XCD x takes the x-th contiguous slice of the
-// (sequence, head, rank) list.  The caller maps rank to a query tile.
+// few rows of a window keep the tiles they stream in L2.  W (from
+// xcd_window) is a multiple of gcd(Hq/Hkv, Hq/8), so the heads reading one
+// K/V head run side by side.  Otherwise XCD x takes the x-th contiguous slice
+// of the (sequence, head, rank) list.  The caller maps rank to a tile.
 FA_HD inline void xcd_work_item(int block, int B, int Hq, int nqt, int W, int& b, int& h,
                                 int& rank) {
   const int xcd = block % kXcds, slot = block / kXcds;
@@ -73,37 +75,6 @@ FA_HD inline void xcd_work_item(int block, int B, int Hq, int nqt, int W, int& b
     b = bhi / Hq;
     h = bhi - b * Hq;
   }
-}
-
-// Block -> (sequence b, head h, tile rank) for the backward kernels, over a
-// grid of ntiles * B * H blocks.  Tile-major order (rank 0 of every head,
-// then rank 1, ...) puts the heaviest tiles first and the lightest in the
-// tail.  When H is a multiple of 8, XCD x takes heads [x H/8, (x+1) H/8) of
-// every sequence (balanced even when packed sequences differ in length) and
-// walks them tile-major, so the tiles it streams stay in its own L2; else,
-// when B*H is, it takes the x-th contiguous slice of the (b, head) rows;
-// else the whole grid is walked tile-major.
-FA_HD inline void bwd_item(int block, int B, int H, int& b, int& h, int& tile) {
-  const int xcd = block % kXcds, slot = block / kXcds;
-  const int rows = B * H;
-  int row;
-  if (H % kXcds == 0) {
-    const int hx = H / kXcds, per = B * hx;
-    tile = slot / per;
-    const int r = slot - tile * per;
-    b = r / hx;
-    h = xcd * hx + (r - b * hx);
-    return;
-  } else if (rows % kXcds == 0) {
-    const int per = rows / kXcds;
-    tile = slot / per;
-    row = xcd * per + (slot - tile * per);
-  } else {
-    tile = block / rows;
-    row = block - tile * rows;
-  }
-  b = row / H;
-  h = row - b * H;
 }
 
 // Keys a query row may see, [kmin(i), kmax(i)], both non-decreasing in i:
