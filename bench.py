@@ -592,6 +592,33 @@ def time_bwd_varlen(dev, reps=10):
             "frac_mfma": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}
 
 
+def time_fp8_d256(dev, reps=20):
+    """fa_fwd_fp8 at D = 256 on the d256 workload's shape (B=2, Hq=Hkv=16,
+    L=4096, causal, e4m3, fp16 O): algorithmic TFLOP/s against the fp8 peak.
+    (Two workgroups share each query tile there, so the MFMAs executed are
+    1.5x the algorithmic ones.)"""
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_fa_amd import workloads as W
+    from exact_tiled_attention_fa_amd.attention import flash_attn_fwd_fp8
+
+    cfg = W.PREFILL["d256"]
+    q8, k8, vt8, ds = W.fp8_inputs(cfg.B, cfg.L, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, cfg.seed)
+    q8, k8, vt8 = q8.to(dev), k8.to(dev), vt8.to(dev)
+    o = torch.empty((cfg.B, cfg.L, cfg.Hq, cfg.D), dtype=torch.float16, device=dev)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.L), dtype=torch.float32, device=dev)
+    sc = float(np.float32(cfg.scale))
+    run = lambda: flash_attn_fwd_fp8(q8, k8, vt8, q_descale=ds, k_descale=ds, v_descale=ds,
+                                     softmax_scale=sc, causal=True, out_dtype=torch.float16,
+                                     out=o, lse=lse)
+    st = _timed_block(run, reps)
+    tf = cfg.flops() / (st["mean"] * 1e-3) / 1e12
+    return {"workload": "d256 shape B=2 Hq=Hkv=16 L=4096 D=256 causal, e4m3 Q/K/V, fp16 O",
+            "ms": st, "alg_flops_per_launch": cfg.flops(), "value": round(tf, 3),
+            "unit": "TFLOP/s", "frac_fp8": round(tf / PEAK_MFMA_FP8_TFLOPS, 4)}
+
+
 def time_fp8(dev, reps=20):
     """fa_fwd_fp8 on the Llama-2-7B-shaped causal workload with e4m3 Q, K, V:
     time (HIP events on the launch stream) and algorithmic TFLOP/s (4*D per
@@ -762,7 +789,9 @@ def main():
             args.config, dev, args.reps or reps, cold)}})
     if args.only == "fp8":
         print("# fp8 forward workload", file=sys.stderr, flush=True)
-        return finish({"fp8": time_fp8(dev, args.reps or 20)})
+        res = time_fp8(dev, args.reps or 20)
+        res["d256"] = time_fp8_d256(dev, args.reps or 20)
+        return finish({"fp8": res})
     if args.only == "bwd":
         print("# backward workload", file=sys.stderr, flush=True)
         res = time_bwd(dev, args.reps or 10)
@@ -878,6 +907,7 @@ def main():
     if do_pf and not args.no_fp8:
         print("# fp8 forward workload", file=sys.stderr, flush=True)
         out["fp8"] = time_fp8(dev)
+        out["fp8"]["d256"] = time_fp8_d256(dev)
     if do_pf and not args.no_bwd:
         print("# backward workload", file=sys.stderr, flush=True)
         out["backward"] = time_bwd(dev)

@@ -146,7 +146,8 @@ fa_status fa_fwd_fp8_ex(const void* q8, const void* k8, const void* vt8, void* o
     return fail(FA_ERR_INVALID_ARGUMENT, "descales must be finite and > 0");
   if (out_dtype != FA_F16 && out_dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "dtype %d is not FA_F16 or FA_BF16", (int)out_dtype);
-  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 head_dim %d not in {64, 128}", D);
+  if (!head_dim_supported(D))
+    return fail(FA_ERR_UNSUPPORTED, "fp8 head_dim %d not in {64, 128, 256}", D);
   // Key tiles read 64 columns of V^T from a 16-aligned start: dense rows hold
   // Lk keys (padded to 64), packed rows total_k keys plus 64 columns of
   // padding.
@@ -162,7 +163,8 @@ fa_status fa_fwd_fp8_ex(const void* q8, const void* k8, const void* vt8, void* o
   const long long rows_k = packed ? (long long)total_k : (long long)B * Lk;
   if (rows_q * Hq > 0x7fffffffLL || rows_k * Hkv > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "B*L*H exceeds 2^31-1 rows");
-  if (((long long)Lq + 127) / 128 * B * Hq > 0x7fffffffLL)
+  // at D = 256 two workgroups share each query tile (128 output dims each)
+  if (((long long)Lq + 127) / 128 * B * Hq * (D / 128 > 1 ? 2 : 1) > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARGUMENT, "grid too large (Lq/128 * B * Hq > 2^31-1)");
   const long long span = rows_q + rows_k;
   const bool windowed = window_left >= 0 || window_right >= 0;
@@ -425,7 +427,8 @@ const char* fa_info(void) {
          "bwd: dQ query-major, dK/dV key-major in pairs of waves, dense and packed, D={64,128,256}; "
          "decode: split-KV, 4 wave64 per (chunk, kv head, 16 heads, sequence), 16-key steps, "
          "mfma_f32_16x16x32 + 16x16x16, logsumexp combine, paged and int8 KV caches; "
-         "version=0.4.0";
+         "fp8 fwd: e4m3 mfma_scale_f32_32x32x64_f8f6f4, D={64,128,256}; "
+         "version=0.5.0";
 }
 
 }  // extern "C"

@@ -86,14 +86,23 @@ __device__ __forceinline__ i32x8 cat(u32x4 a, u32x4 b) {
                  (int)b[3]};
 }
 
+// Output head dimensions one workgroup owns: all of them up to D = 128; at
+// D = 256 two workgroups share a query tile, each forming the full scores and
+// probabilities and the P V product for 128 of the output dimensions (so its
+// accumulator is the D = 128 one: the 256-wide one does not fit beside the
+// operands in a wave's registers).
+template <int D> struct Fp8Dv { static constexpr int value = D <= 128 ? D : 128; };
+
 template <int D, typename OT, bool CAUSAL>
 __global__ __launch_bounds__(kPT, 2)
 void fwd_fp8_kernel(const Fp8Params prm) {
+  constexpr int DV = Fp8Dv<D>::value;  // output dimensions of this workgroup
+  constexpr int NSPLIT = D / DV;       // workgroups per query tile
   constexpr int KT = kPBN * D;   // bytes per K tile
-  constexpr int VTB = D * kPBN;  // bytes per V^T tile
+  constexpr int VTB = DV * kPBN; // bytes per V^T tile
   constexpr int CK = D / 16;     // 16-byte chunks per K row
   constexpr int NK = kPBN * CK / kPT;
-  constexpr int NV = D * 4 / kPT;
+  constexpr int NV = DV * 4 / kPT;
   static_assert(NK >= 1 && NV >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t sK0[KT];
   __shared__ __attribute__((aligned(16))) uint8_t sV0[VTB];
@@ -106,8 +115,13 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   const int l32 = lane & 31, hf = lane >> 5;
 
   const int nqt = (prm.Lq + kPBM - 1) / kPBM;
+  // the grid holds NSPLIT copies of the nqt * B * Hq work items, one per
+  // range of output dimensions
+  const int nitems = nqt * B * Hq;
+  const int split = (int)blockIdx.x / nitems;
+  const int dv0 = split * DV;
   int b, h, qt;
-  xcd_work_item((int)blockIdx.x, B, Hq, nqt, prm.xcd_w, b, h, qt);
+  xcd_work_item((int)blockIdx.x - split * nitems, B, Hq, nqt, prm.xcd_w, b, h, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int kvh = h / (Hq / Hkv);
   // This sequence's rows.  Packed offsets are clamped into the tensors so
@@ -147,8 +161,9 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   // Hkv, D], V^T [Hkv, D, vt_stride] with key row r of K at column r
   const uint8_t* Kb = prm.cu_q ? prm.K + (long)c0 * kstride + (long)kvh * D
                                : prm.K + (long)b * Lk * kstride + (long)kvh * D;
-  const uint8_t* Vb = prm.cu_q ? prm.VT + (long)kvh * D * (long)prm.vt_stride + c0
-                               : prm.VT + ((long)b * Hkv + kvh) * D * (long)prm.vt_stride;
+  const uint8_t* Vb = (prm.cu_q ? prm.VT + (long)kvh * D * (long)prm.vt_stride + c0
+                                : prm.VT + ((long)b * Hkv + kvh) * D * (long)prm.vt_stride) +
+                     (long)dv0 * prm.vt_stride;  // this workgroup's output dimensions
 
   // Q^T operand: lane holds query qrow, dims 64m + 32hf .. +31 for MFMA m.
   i32x8 qf[D / 64];
@@ -211,9 +226,9 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   // A-operand rows of the S^T MFMA: lane i reads K row 16((i/4)%2) + 4(i/8) + i%4.
   const int arow = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
 
-  f32x16 acc[D / 32];
+  f32x16 acc[DV / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  for (int i = 0; i < DV / 32; ++i) acc[i] = (f32x16){};
   float m_ref = -INFINITY, l_part = 0.f;
   const float scale2 = prm.scale2, thr = prm.thr;
 
@@ -254,7 +269,7 @@ void fwd_fp8_kernel(const Fp8Params prm) {
       const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast((m_ref - m_new) * scale2);
       l_part *= alpha;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      for (int i = 0; i < DV / 32; ++i) acc[i] *= alpha;
       m_ref = m_new;
     }
     // 256 P (the factor keeps the e4m3 rounding clear of subnormals; it enters
@@ -278,7 +293,7 @@ void fwd_fp8_kernel(const Fp8Params prm) {
     }
     // O^T += V^T P^T: A = V^T row d, keys 16hf .. +15 and 32+16hf .. +15
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < DV / 32; ++db) {
       const int d = 32 * db + l32;
       const u32x4 a0 = *reinterpret_cast<const u32x4*>(sV + d * kPBN + 16 * (hf ^ swz_v8(d)));
       const u32x4 a1 =
@@ -308,19 +323,19 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   // rows [32][D] of 16-bit values with 16-byte chunks XOR-swizzled by row) and
   // written as whole rows with non-temporal stores; lse = ln2 * (m*scale2 +
   // log2 l).
-  constexpr int CPR = D / 8;
+  constexpr int CPR = DV / 8;
   constexpr int OSW = CPR < 16 ? CPR - 1 : 15;
-  static_assert(32 * D * 2 <= KT, "O stage");
+  static_assert(32 * DV * 2 <= KT, "O stage");
   __syncthreads();  // every copy has landed and all waves are done with the tiles
   uint16_t* so = reinterpret_cast<uint16_t*>((w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * db + 8 * g + 4 * hf;
       const u32x2 val = {Ops<OT>::pack2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
                          Ops<OT>::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2*>(so + l32 * D + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
+      *reinterpret_cast<u32x2*>(so + l32 * DV + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
     }
   __syncthreads();
 #pragma unroll
@@ -330,10 +345,10 @@ void fwd_fp8_kernel(const Fp8Params prm) {
     const int q = qw0 + row;
     if (q < Lq)
       __builtin_nontemporal_store(
-          *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))),
-          reinterpret_cast<u32x4*>(prm.O + ((long)qs + q) * qstride + (long)h * D + 8 * c));
+          *reinterpret_cast<const u32x4*>(so + row * DV + 8 * (c ^ (row & OSW))),
+          reinterpret_cast<u32x4*>(prm.O + ((long)qs + q) * qstride + (long)h * D + dv0 + 8 * c));
   }
-  if (hf == 0 && qrow < Lq)  // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
+  if (split == 0 && hf == 0 && qrow < Lq)  // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
     __builtin_nontemporal_store(
         l > 0.f ? (m_ref * scale2 + __builtin_log2f(l) - 8.f) * kLn2 : -INFINITY,
         prm.LSE + (prm.cu_q ? (long)h * prm.total_q + qs + qrow : ((long)b * Hq + h) * Lq + qrow));
@@ -367,7 +382,7 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
   const int nqt = (a.Lq + kPBM - 1) / kPBM;
   // blocks resident per CU at this kernel's register use: 4 (D=64), 3 (D=128)
   p.xcd_w = xcd_window(a.B, a.Hq, a.Hkv, nqt, D == 64 ? 4 : 3);
-  const dim3 grid((unsigned)((long)nqt * a.B * a.Hq));
+  const dim3 grid((unsigned)((long)nqt * a.B * a.Hq * (D / Fp8Dv<D>::value)));
   if (a.causal)
     hipLaunchKernelGGL((fwd_fp8_kernel<D, OT, true>), grid, dim3(kPT), 0, stream, p);
   else
@@ -380,6 +395,7 @@ hipError_t launch_fp8_out(const Fp8Args& a, hipStream_t stream) {
   switch (a.D) {
     case 64: return launch_fp8_t<64, OT>(a, stream);
     case 128: return launch_fp8_t<128, OT>(a, stream);
+    case 256: return launch_fp8_t<256, OT>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

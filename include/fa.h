@@ -131,7 +131,9 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
  *               >= Lk; columns Lk .. vt_stride-1 are read and must hold finite
  *               codes (zeros), their probabilities being 0.
  *   o, lse      as fa_fwd; o in out_dtype.
- *   D           64 or 128.
+ *   D           64, 128 or 256 (at 256 two workgroups share each query tile,
+ *               each forming the scores and probabilities and the P V
+ *               product for 128 of the output dimensions).
  *   scale       softmax scale applied to the real (descaled) scores.
  *   q_descale, k_descale, v_descale   finite, > 0.
  *   other arguments as in fa_fwd_ex.  D * vt_stride must be below 2^32.

@@ -270,7 +270,7 @@ def fp8(**kw):
     (dict(vts=64, Lk=65), _abi.FA_ERR_INVALID_ARGUMENT, "vt_stride=64"),
     (dict(qd=0.0), _abi.FA_ERR_INVALID_ARGUMENT, "descales"),
     (dict(vd=float("nan")), _abi.FA_ERR_INVALID_ARGUMENT, "descales"),
-    (dict(D=256), _abi.FA_ERR_UNSUPPORTED, "fp8 head_dim 256"),
+    (dict(D=96), _abi.FA_ERR_UNSUPPORTED, "fp8 head_dim 96"),
     (dict(dtype=5), _abi.FA_ERR_UNSUPPORTED, "dtype 5"),
     (dict(Hq=3, Hkv=2), _abi.FA_ERR_INVALID_ARGUMENT, "not a multiple"),
 ])
@@ -297,7 +297,7 @@ PACKED8 = dict(cu_q=A16, cu_k=A16, B=2, Lq=8, Lk=8, total_q=16, total_k=16, vts=
     (dict(PACKED8, total_q=0), _abi.FA_ERR_INVALID_ARGUMENT, "total_q=0"),
     (dict(PACKED8, vts=64), _abi.FA_ERR_INVALID_ARGUMENT, "vt_stride=64"),
     (dict(PACKED8, vts=100), _abi.FA_ERR_INVALID_ARGUMENT, "multiple of 64"),
-    (dict(PACKED8, D=256), _abi.FA_ERR_UNSUPPORTED, "fp8 head_dim 256"),
+    (dict(PACKED8, D=32), _abi.FA_ERR_UNSUPPORTED, "fp8 head_dim 32"),
     (dict(PACKED8, total_q=1 << 30, Hq=4, Hkv=1), _abi.FA_ERR_INVALID_ARGUMENT, "2^31-1"),
 ])
 def test_fp8_ex_rejects(lib, kw, status, text):
@@ -307,7 +307,7 @@ def test_fp8_ex_rejects(lib, kw, status, text):
 
 def test_fp8_is_fp8_ex_without_offsets(lib):
     """fa_fwd_fp8 validates exactly as fa_fwd_fp8_ex with NULL offsets."""
-    for kw in (dict(vt=None), dict(vts=32), dict(vts=64, Lk=65), dict(qd=0.0), dict(D=256),
+    for kw in (dict(vt=None), dict(vts=32), dict(vts=64, Lk=65), dict(qd=0.0), dict(D=96),
                dict(dtype=5), dict(Hq=3, Hkv=2)):
         st1 = fp8(**kw)
         e1 = _abi.fa_last_error()

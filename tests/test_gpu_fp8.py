@@ -76,7 +76,7 @@ RAGGED = [(1, 1), (17, 17), (63, 63), (64, 64), (65, 65), (128, 128), (129, 129)
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("Lq,Lk", RAGGED, ids=[f"{a}x{b}" for a, b in RAGGED])
 def test_fp8_ragged(Lq, Lk, D, causal, gpu):
     check(1, Lq, Lk, 4, 2, D, causal, seed=Lq * 13 + Lk + D, gpu=gpu)
@@ -109,6 +109,20 @@ def test_fp8_full_size(gpu):
     slice."""
     cfg = W.PREFILL["llama7b"]
     check(cfg.B, cfg.L, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, True, seed=cfg.seed, gpu=gpu)
+
+
+def test_fp8_d256_full_size(gpu):
+    """The D = 256 workload's shape (B=2, H=16, L=4096, causal) in fp8; at
+    D = 256 two workgroups share each query tile, 128 output dimensions each.
+    The oracle computes every (batch, head) slice."""
+    cfg = W.PREFILL["d256"]
+    check(cfg.B, cfg.L, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, True, seed=cfg.seed, gpu=gpu,
+          out_dtype=torch.float16)
+
+
+@pytest.mark.parametrize("window", [(0, 0), (64, -1)], ids=["w0_0", "w64_"])
+def test_fp8_d256_gqa_window(window, gpu):
+    check(2, 300, 333, 8, 2, 256, True, seed=66 + window[0], gpu=gpu, window=window)
 
 
 def test_fp8_deterministic(gpu):
@@ -157,7 +171,7 @@ def check_varlen(lens_q, lens_k, Hq, Hkv, D, causal, seed, gpu, *, window=(-1, -
 
 @pytest.mark.parametrize("window", [(-1, -1), (32, 8)], ids=["nowin", "win"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("mix", range(len(VARLEN_MIXES)))
 def test_fp8_varlen(mix, D, causal, window, gpu):
     lq, lk = VARLEN_MIXES[mix]

@@ -162,7 +162,7 @@ def test_random_forward_fp8(case, gpu):
     B = int(rng.integers(1, 3))
     Lq, Lk = (int(x) for x in rng.integers(1, 500, 2))
     Hq, Hkv = draw_heads(rng)
-    D = int(rng.choice([64, 128]))
+    D = int(rng.choice([64, 128, 256]))
     causal = bool(rng.integers(0, 2))
     window = draw_window(rng)
     scale = float(rng.uniform(-0.3, 0.3)) if rng.random() < 0.2 else None
@@ -209,7 +209,7 @@ def test_random_forward_fp8_packed(case, gpu):
     lens_q = draw_lens(rng, B, 300)
     lens_k = lens_q if rng.random() < 0.5 else draw_lens(rng, B, 300)
     Hq, Hkv = draw_heads(rng)
-    D = int(rng.choice([64, 128]))
+    D = int(rng.choice([64, 128, 256]))
     causal = bool(rng.integers(0, 2))
     window = draw_window(rng)
     out_dtype = DTYPES[int(rng.integers(0, 2))]
