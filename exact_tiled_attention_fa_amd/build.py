@@ -30,8 +30,12 @@ OBJ_DIR = ROOT / "_build"
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_decode_noalloc.hip", "fa_bwd.hip",
            "fa_fwd_fp8.hip"]
 PROBE_SOURCES = ["probe/mfma_probe.hip", "probe/rate_probe.hip", "probe/rate_probe_vgpr.hip"]
-# per-source extra flags
-EXTRA_FLAGS = {"probe/rate_probe_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The decode kernels keep their MFMA accumulators in
+# ArchVGPRs: with the compiler's default split they live in AccVGPRs across
+# the key loop and are copied out and back every step (about 300 moves per
+# kernel), and the int8 instances need a fourth of the file more registers.
+EXTRA_FLAGS = {"probe/rate_probe_vgpr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "fa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 PROBE_LIB = OUT_DIR / "libfa_probe.so"
 ARCH = "gfx950"
 

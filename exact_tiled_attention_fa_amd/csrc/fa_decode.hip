@@ -51,9 +51,9 @@ namespace fa {
 namespace {
 
 constexpr int kKS = kDecodeKeysPerStep;  // keys per step (one 16-key MFMA block)
-
-constexpr int kDW = 4;                   // waves per split workgroup
 static_assert(kKS == 16, "the decode MFMA layout assumes 16-key steps");
+
+constexpr int kDW = 4;  // waves per split workgroup
 
 // XOR on the 16-byte chunk index of row r of a V tile: a transpose read of
 // one 32-lane half touches 8 consecutive rows x 32 bytes, spread over banks.
@@ -112,8 +112,12 @@ void decode_split_kernel(const SplitParams prm) {
   constexpr int VT = kKS * D;          // elements per V tile
   // 16-byte V loads per lane per step (8 16-bit or 16 int8 elements each)
   constexpr int NVL = VI8 ? kKS * D / 16 / 64 : kKS * CPR / 64;
-  constexpr int MERGE = 16 * D * 2;    // per-wave merge room in elements (16 heads x D floats)
-  constexpr int WS = VT > MERGE ? VT : MERGE;
+  // The waves' outputs (16 heads x D floats each) are merged through the V
+  // tiles' room (16 x D 16-bit values each) in two passes over the head dims.
+  constexpr int MP = 2;
+  constexpr int DP = D / MP;
+  constexpr int WS = VT;
+  static_assert(16 * DP * 2 <= WS && DP % 16 == 0, "merge room");
   __shared__ __attribute__((aligned(16))) uint16_t sV[kDW][WS];
   __shared__ float sL[kDW][16];
   // Per-wave K tile [16][D] (16-bit or int8 codes), 16-byte chunks XOR-swizzled by row.
@@ -121,8 +125,9 @@ void decode_split_kernel(const SplitParams prm) {
   constexpr int KLPR = D * KEB / 16;       // 16-byte K loads per row
   constexpr int NKL = kKS * KLPR / 64;     // 16-byte K loads per lane per step
   constexpr int KSW = (KLPR < 16 ? KLPR : 16) - 1;
-  static_assert(NKL >= 1, "K tile shape");
+  static_assert(NKL >= 1 && NVL >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t sKt[kDW][kKS * D * KEB];
+  __shared__ __attribute__((aligned(16))) float sSc[kDW][64];  // int8 row scales of a step
 
   const int split = blockIdx.x;
   const int b = blockIdx.z;
@@ -213,7 +218,7 @@ void decode_split_kernel(const SplitParams prm) {
   // of 16-bit elements), with non-temporal loads, and staged through the
   // wave's LDS tile: the MFMA operand layout would fetch half a cache line
   // per instruction.
-  auto kload = [&](const StepRows& st, u32x4 (&kx)[NKL], f32x4& ksc) {
+  auto kload = [&](const StepRows& st, u32x4 (&kx)[NKL]) {
     const KE* kr = Kb + st.row0 * kstride;
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
@@ -221,13 +226,10 @@ void decode_split_kernel(const SplitParams prm) {
       kx[i] = stream_load(
           reinterpret_cast<const u32x4*>(kr + row_off(st, P / KLPR) + (16 / KEB) * (P % KLPR)));
     }
-    // scales of keys first + 4*q4 .. +3 (the score layout below); slots past
-    // the chunk end hold anything and are masked
-    if constexpr (KI8) ksc = *reinterpret_cast<const f32x4*>(prm.ksc + st.srow + 4 * q4);
   };
   constexpr int VEPL = VI8 ? 16 : 8;  // elements per 16-byte V load
   constexpr int VLPR = D / VEPL;      // 16-byte V loads per row
-  auto vload = [&](const StepRows& st, u32x4 (&vx)[NVL], f32x4& vsc) {
+  auto vload = [&](const StepRows& st, u32x4 (&vx)[NVL]) {
     const VE* vr = Vb + st.row0 * kstride;
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
@@ -235,13 +237,27 @@ void decode_split_kernel(const SplitParams prm) {
       vx[i] = stream_load(
           reinterpret_cast<const u32x4*>(vr + row_off(st, P / VLPR) + VEPL * (P % VLPR)));
     }
-    if constexpr (VI8) vsc = *reinterpret_cast<const f32x4*>(prm.vsc + st.srow + 4 * q4);
   };
-  auto load_step = [&](int j, u32x4 (&kx)[NKL], f32x4& ksc, u32x4 (&vx)[NVL], f32x4& vsc) {
+  // Int8 sides: a step's row scales, one per lane (lane l holds the scale of
+  // key l % 16 of side (l / 16) % NSD, the K side first).  They pass through
+  // the wave's LDS like the tiles, which costs one register per step instead
+  // of four per side.  Scales of keys past the chunk end hold anything and
+  // are masked.
+  constexpr int NSD = (KI8 ? 1 : 0) + (VI8 ? 1 : 0);
+  const bool s_kside = KI8 && (lane / kKS) % (NSD ? NSD : 1) == 0;
+  const float* const s_base = s_kside ? prm.ksc : prm.vsc;
+  struct StepRegs {  // one step's rows in registers
+    u32x4 k[NKL];
+    u32x4 v[NVL];
+    float sc;
+  };
+  auto load_step = [&](int j, StepRegs& r) {
     const StepRows st = step_rows(j);
-    kload(st, kx, ksc);
-    vload(st, vx, vsc);
+    kload(st, r.k);
+    vload(st, r.v);
+    if constexpr (NSD > 0) r.sc = s_base[st.srow + l16];
   };
+  float* const ss = sSc[w];
   uint16_t* const sv = sV[w];
   uint8_t* const sk = sKt[w];
   auto kstore = [&](const u32x4 (&kx)[NKL]) {
@@ -268,8 +284,8 @@ void decode_split_kernel(const SplitParams prm) {
       }
     }
   };
-  // V^T read for head-dim block db: row 4*q4 + l16/4, columns 16db + 4*(l16%4)
-  // .. +3, so lane l16 gets column 16db + l16 of keys 4*q4 .. 4*q4+3.
+  // V^T read for head-dim block db: row 4*q4 + l16/4, columns 16db +
+  // 4*(l16%4) .. +3, so lane l16 gets column 16db + l16 of keys 4*q4 .. 4*q4+3.
   const int vr = 4 * q4 + (l16 >> 2);
   int voff[D / 16];
 #pragma unroll
@@ -284,12 +300,12 @@ void decode_split_kernel(const SplitParams prm) {
   float m_ref = -INFINITY;
   float l_part = 0.f;
 
-  auto compute = [&](int j, const u32x4 (&kx)[NKL], const f32x4& ksc, const u32x4 (&vx)[NVL],
-                     const f32x4& vsc) {
-    // the previous step's reads of both tiles are done (in-order LDS)
-    kstore(kx);
-    vstore(vx);
-    // S^T: keys 4*q4 + r (rows) x heads (columns l16); lane (l16, q4) takes
+  auto compute = [&](int j, const StepRegs& r) {
+    // the previous step's reads of the tiles and scales are done (in-order LDS)
+    kstore(r.k);
+    vstore(r.v);
+    if constexpr (NSD > 0) ss[lane] = r.sc;
+    // S^T: keys 4*q4 + i (rows) x heads (columns l16); lane (l16, q4) takes
     // dims 32*ks + 8*q4 .. +7 of key row l16.
     f32x4 s = (f32x4){};
 #pragma unroll
@@ -304,13 +320,14 @@ void decode_split_kernel(const SplitParams prm) {
         s = Ops<T>::mfma16(a, qf[ks], s);
       }
     }
-    if constexpr (KI8) s *= ksc;  // each key row's scale
-    const int lim = k1 - 1 - (k0 + kKS * j) - 4 * q4;  // key offset r visible iff <= lim
+    if constexpr (KI8)  // each key row's scale (keys 4*q4 .. +3)
+      s *= *reinterpret_cast<const f32x4*>(ss + 4 * q4);
+    const int lim = k1 - 1 - (k0 + kKS * j) - 4 * q4;  // key offset i visible iff <= lim
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (r > lim) s[r] = -INFINITY;
-      mx = fmaxf(mx, s[r]);
+    for (int i = 0; i < 4; ++i) {
+      if (i > lim) s[i] = -INFINITY;
+      mx = fmaxf(mx, s[i]);
     }
     mx = fmaxf(mx, xor16(mx));
     mx = max_halves(mx);
@@ -332,10 +349,10 @@ void decode_split_kernel(const SplitParams prm) {
     l_part += (p0 + p1) + (p2 + p3);  // unrounded: lse carries no 16-bit rounding
     u32x2 bop;
     if constexpr (VI8) {  // each value row's scale, folded into its probability
-      f32x4 vs = vsc;
+      f32x4 vs = *reinterpret_cast<const f32x4*>(ss + kKS * (NSD - 1) + 4 * q4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r > lim) vs[r] = 0.f;  // masked keys: their slot's scale may be anything
+      for (int i = 0; i < 4; ++i)
+        if (i > lim) vs[i] = 0.f;  // masked keys: their slot's scale may be anything
       bop = (u32x2){Ops<T>::pack2(p0 * vs[0], p1 * vs[1]), Ops<T>::pack2(p2 * vs[2], p3 * vs[3])};
     } else
       bop = (u32x2){Ops<T>::pack2(p0, p1), Ops<T>::pack2(p2, p3)};
@@ -348,22 +365,20 @@ void decode_split_kernel(const SplitParams prm) {
   // step computes.  The request is unconditional (past the last step it
   // re-reads the chunk's final row, a cache hit) so that the number of loads
   // in flight, and thus each wait, is the same on every path.
-  u32x4 kA[NKL], kB[NKL];
-  u32x4 vA[NVL], vB[NVL];
-  f32x4 kscA = {}, kscB = {}, vscA = {}, vscB = {};
-  load_step(w, kA, kscA, vA, vscA);  // (a wave with no step reads the chunk's last step, unused)
+  StepRegs rA, rB;
+  load_step(w, rA);  // (a wave with no step reads the chunk's last step, unused)
   // The scheduling barriers keep each request ahead of the wait for the step
   // being computed, so two steps are in flight while that wait lasts.  (A
-  // third step in flight costs the registers of a second wave per SIMD and
-  // measured slower, for int8 caches too.)
+  // third step in flight, or 32-key steps for int8 caches, cost a wave per
+  // SIMD in registers or serialise each wave further, and measured slower.)
   for (int i = 0; i < my_steps; i += 2) {
-    load_step(w + kDW * (i + 1), kB, kscB, vB, vscB);
+    load_step(w + kDW * (i + 1), rB);
     __builtin_amdgcn_sched_barrier(0);
-    compute(w + kDW * i, kA, kscA, vA, vscA);
+    compute(w + kDW * i, rA);
     if (i + 1 >= my_steps) break;
-    load_step(w + kDW * (i + 2), kA, kscA, vA, vscA);
+    load_step(w + kDW * (i + 2), rA);
     __builtin_amdgcn_sched_barrier(0);
-    compute(w + kDW * (i + 1), kB, kscB, vB, vscB);
+    compute(w + kDW * (i + 1), rB);
   }
 
   // Merge the waves: full row sums, per-wave normalised output and lse2 to LDS.
@@ -373,32 +388,37 @@ void decode_split_kernel(const SplitParams prm) {
   const float lse2 = l > 0.f ? m_ref * scale2 + __builtin_log2f(l) : -INFINITY;
   __syncthreads();  // all waves are done with their V tiles
   float* sO = reinterpret_cast<float*>(&sV[0][0]);
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    *reinterpret_cast<f32x4*>(sO + w * (WS / 2) + l16 * D + 16 * db + 4 * q4) = acc[db] * inv;
   if (q4 == 0) sL[w][l16] = lse2;
-  __syncthreads();
-  for (int e = tid; e < 16 * D; e += 64 * kDW) {
-    const int hs = e / D, d = e - hs * D;
-    if (hg * 16 + hs >= g) continue;
-    float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kDW; ++v) M = fmaxf(M, sL[v][hs]);
-    float tot = 0.f, o = 0.f;
-    if (M != -INFINITY) {
+  for (int mp = 0; mp < MP; ++mp) {
+    if (mp) __syncthreads();  // the previous pass's reads are done
 #pragma unroll
-      for (int v = 0; v < kDW; ++v) {
-        const float lv = sL[v][hs];
-        if (lv == -INFINITY) continue;
-        const float wt = exp2_fast(lv - M);
-        tot += wt;
-        o += wt * sO[v * (WS / 2) + hs * D + d];
+    for (int db = 0; db < DP / 16; ++db)
+      *reinterpret_cast<f32x4*>(sO + w * (WS / 2) + l16 * DP + 16 * db + 4 * q4) =
+          acc[mp * (DP / 16) + db] * inv;
+    __syncthreads();
+    for (int e = tid; e < 16 * DP; e += 64 * kDW) {
+      const int hs = e / DP, d = e - hs * DP;
+      if (hg * 16 + hs >= g) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kDW; ++v) M = fmaxf(M, sL[v][hs]);
+      float tot = 0.f, o = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < kDW; ++v) {
+          const float lv = sL[v][hs];
+          if (lv == -INFINITY) continue;
+          const float wt = exp2_fast(lv - M);
+          tot += wt;
+          o += wt * sO[v * (WS / 2) + hs * DP + d];
+        }
+        o /= tot;
       }
-      o /= tot;
+      const long pi = pbase + (long)hs * S;
+      __builtin_nontemporal_store(o, Opart + pi * D + mp * DP + d);  // read once, by the merge
+      if (mp == 0 && d == 0) Lpart[pi] = M != -INFINITY ? M + __builtin_log2f(tot) : -INFINITY;
     }
-    const long pi = pbase + (long)hs * S;
-    __builtin_nontemporal_store(o, Opart + pi * D + d);  // read once, by the merge
-    if (d == 0) Lpart[pi] = M != -INFINITY ? M + __builtin_log2f(tot) : -INFINITY;
   }
 }
 
@@ -459,7 +479,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   // <= 127 * scale, the same bound the output needs).
   p.thr = (VI8 && std::is_same<T, f16_t>::value) ? 0.f : 8.f / p.scale2;
   p.qxor = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, PAGED, KI8, VI8>), dim3(a.num_splits, a.Hkv * nhg, a.B),
+  hipLaunchKernelGGL((decode_split_kernel<T, D, PAGED, KI8, VI8>),
+                     dim3(a.num_splits, a.Hkv * nhg, a.B),
                      dim3(64 * kDW), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
