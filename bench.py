@@ -75,6 +75,8 @@ def parse():
     p.add_argument("--no-configs", action="store_true",
                    help="skip the other prefill workloads (long-context, D=256, encoder, tiny)")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward workload")
+    p.add_argument("--bwd-workload", choices=["llama7b", "varlen16"], default=None,
+                   help="with --only bwd: time only this backward workload")
     p.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward workload")
     p.add_argument("--probe", action="store_true",
                    help="also time the matrix-core probe (libfa_probe.so) on the prefill's Q "
@@ -794,8 +796,9 @@ def main():
         return finish({"fp8": res})
     if args.only == "bwd":
         print("# backward workload", file=sys.stderr, flush=True)
-        res = time_bwd(dev, args.reps or 10)
-        res["varlen16"] = time_bwd_varlen(dev, args.reps or 10)
+        res = time_bwd(dev, args.reps or 10) if args.bwd_workload in (None, "llama7b") else {}
+        if args.bwd_workload in (None, "varlen16"):
+            res["varlen16"] = time_bwd_varlen(dev, args.reps or 10)
         return finish({"backward": res})
     if args.only == "paged":
         print("# paged decode workloads", file=sys.stderr, flush=True)
