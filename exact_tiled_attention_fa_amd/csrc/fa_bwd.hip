@@ -77,20 +77,18 @@ struct BwdParams {
 };
 
 // XOR on a row's 16-byte chunk index in the LDS tiles.  Each tile is read two
-// ways: by rows (16 lanes read one logical chunk of 16 consecutive rows) and
-// by transpose reads (16 lanes read logical chunks 2m and 2m+1 of 4
-// consecutive rows, 8 bytes each).  At D >= 128 a row spans all 64 banks, so
-// the 16 rows need 16 distinct XOR values, and the 4 rows' values must differ
-// above bit 0 so that their chunk pairs {x, x^1} are disjoint: the XOR value
-// is the row's low four bits permuted (r1 r0 -> bits 2 1, r2 -> bit 0, r3
-// stays).  At D = 64 two rows share the banks (odd rows on the upper half),
-// so the value comes from r >> 1 with its two low bits swapped.  (r & 15
-// satisfies the row reads only: the transpose reads then met two-way bank
-// conflicts.)
+// ways: by rows (16 lanes, 256 bytes, read one logical chunk of 16 consecutive
+// rows) and by transpose reads (32 lanes, 256 bytes, read logical chunks
+// 4m .. 4m+3 of 4 consecutive rows, 8 bytes each).  At D >= 128 a row spans
+// all 64 banks, so the 16 rows need 16 distinct XOR values, and the 4 rows'
+// values must differ above bit 1 so that their chunk quads are disjoint: the
+// value swaps the two 2-bit halves of the row's low four bits.  At D = 64 two
+// rows share the banks (odd rows on the upper half), so the value is a
+// permutation of r >> 1 whose bit 2 separates rows 2 apart.
 template <int D> __device__ __forceinline__ int swz_b(int r) {
-  if constexpr (D >= 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   const int x = (r >> 1) & 7;
-  return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+  return ((x & 1) << 2) | (x >> 1);
 }
 
 // Rows of sequence b: queries qs .. qs+Lq-1 and keys ks .. ks+Lk-1.  Packed

@@ -55,10 +55,23 @@ static_assert(kKS == 16, "the decode MFMA layout assumes 16-key steps");
 
 constexpr int kDW = 4;  // waves per split workgroup
 
-// XOR on the 16-byte chunk index of row r of a V tile: a transpose read of
-// one 32-lane half touches 8 consecutive rows x 32 bytes, spread over banks.
+// LDS bank layout (64 banks of 4 bytes; an access is served 256 bytes at a
+// time: 16 lanes of a 16-byte access, 32 of an 8-byte one).
+//
+// XOR on the 16-byte chunk index of row r of a tile whose rows hold N chunks,
+// read 16 consecutive rows at one logical chunk: rows sharing a 256-byte bank
+// row (16 / N of them when N < 16) get distinct chunks.
+template <int N> __device__ __forceinline__ int row_xor(int r) {
+  return N >= 16 ? (r & 15) : ((r / (16 / N)) & (N - 1));
+}
+
+// XOR on the 16-byte chunk index of row r of a V tile.  A transpose read of 32
+// lanes touches chunks 2m, 2m+1 of 8 consecutive rows, so bits above 0 spread
+// the rows' chunk pairs; bit 0 alternates between the rows a 16-lane store of
+// widened int8 codes covers together (its first store writes chunk 2c of each
+// row), so those rows land on even and odd chunks.
 template <int D> __device__ __forceinline__ int swz_dv(int r) {
-  return D == 64 ? 2 * ((r >> 1) & 3) : 2 * (r & 7);
+  return D == 64 ? (2 * ((r >> 1) & 3) | ((r >> 1) & 1)) : (2 * (r & 7) | (r & 1));
 }
 
 struct SplitParams {
@@ -124,7 +137,6 @@ void decode_split_kernel(const SplitParams prm) {
   constexpr int KEB = KI8 ? 1 : 2;         // bytes per cached K element
   constexpr int KLPR = D * KEB / 16;       // 16-byte K loads per row
   constexpr int NKL = kKS * KLPR / 64;     // 16-byte K loads per lane per step
-  constexpr int KSW = (KLPR < 16 ? KLPR : 16) - 1;
   static_assert(NKL >= 1 && NVL >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t sKt[kDW][kKS * D * KEB];
   __shared__ __attribute__((aligned(16))) float sSc[kDW][64];  // int8 row scales of a step
@@ -265,7 +277,7 @@ void decode_split_kernel(const SplitParams prm) {
     for (int i = 0; i < NKL; ++i) {
       const int P = 64 * i + lane;
       const int r = P / KLPR, c = P % KLPR;
-      *reinterpret_cast<u32x4*>(sk + 16 * (r * KLPR + (c ^ (r & KSW)))) = kx[i];
+      *reinterpret_cast<u32x4*>(sk + 16 * (r * KLPR + (c ^ row_xor<KLPR>(r)))) = kx[i];
     }
   };
   // Row-major V tile [16][D] of 16-bit values with 16-byte chunks
@@ -312,11 +324,11 @@ void decode_split_kernel(const SplitParams prm) {
     for (int ks = 0; ks < D / 32; ++ks) {
       if constexpr (KI8) {
         const u32x2 a = *reinterpret_cast<const u32x2*>(
-            sk + 16 * (l16 * KLPR + ((2 * ks + (q4 >> 1)) ^ (l16 & KSW))) + 8 * (q4 & 1));
+            sk + 16 * (l16 * KLPR + ((2 * ks + (q4 >> 1)) ^ row_xor<KLPR>(l16))) + 8 * (q4 & 1));
         s = Ops<T>::mfma16(widen8<T>(a), qf[ks], s);
       } else {
         const u32x4 a = *reinterpret_cast<const u32x4*>(
-            sk + 16 * (l16 * KLPR + ((4 * ks + q4) ^ (l16 & KSW))));
+            sk + 16 * (l16 * KLPR + ((4 * ks + q4) ^ row_xor<KLPR>(l16))));
         s = Ops<T>::mfma16(a, qf[ks], s);
       }
     }
@@ -394,7 +406,8 @@ void decode_split_kernel(const SplitParams prm) {
     if (mp) __syncthreads();  // the previous pass's reads are done
 #pragma unroll
     for (int db = 0; db < DP / 16; ++db)
-      *reinterpret_cast<f32x4*>(sO + w * (WS / 2) + l16 * DP + 16 * db + 4 * q4) =
+      *reinterpret_cast<f32x4*>(sO + w * (WS / 2) + l16 * DP +
+                                4 * ((4 * db + q4) ^ row_xor<DP / 4>(l16))) =
           acc[mp * (DP / 16) + db] * inv;
     __syncthreads();
     for (int e = tid; e < 16 * DP; e += 64 * kDW) {
@@ -411,7 +424,7 @@ void decode_split_kernel(const SplitParams prm) {
           if (lv == -INFINITY) continue;
           const float wt = exp2_fast(lv - M);
           tot += wt;
-          o += wt * sO[v * (WS / 2) + hs * DP + d];
+          o += wt * sO[v * (WS / 2) + hs * DP + 4 * ((d >> 2) ^ row_xor<DP / 4>(hs)) + (d & 3)];
         }
         o /= tot;
       }
