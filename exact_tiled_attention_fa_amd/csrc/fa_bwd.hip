@@ -279,8 +279,9 @@ void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
 
   const int Hq = p.Hq;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index, wave-uniform (in an SGPR): so are the bounds derived from it
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wu = w;
   const int l32 = lane & 31, hf = lane >> 5;
   const int nqt = (p.Lq + kBM - 1) / kBM;
   int b, h, tt;
@@ -596,10 +597,19 @@ void bwd_dkdv_kernel(const BwdParams p) {
     // have lse2 = +inf: P = 0 as well).
     const int qlast = min(q0 + BQ, Lq) - 1;
     if (!(kw0 >= kmin(qlast) && kw0 + kBR - 1 <= kmax(q0) && kw0 + kBR <= Lk)) {
+      // query q0 + 4hf + off sees `key` iff lo <= off <= hi (kmin(i) <= key <=
+      // kmax(i) solved for i), so each element is one compare pair against a
+      // constant offset, with no branch
+      const int base = key - shift - q0 - 4 * hf;
+      int lo = -(1 << 30);
+      const int hi = wl < 0 ? (1 << 30) : base + wl;
+      if (CAUSAL) lo = max(lo, base);
+      if (wr >= 0) lo = max(lo, base - wr);
+      if (key >= Lk) lo = 1 << 30;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key < kmin(qi) || key > kmax(qi)) s[r] = -INFINITY;
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off < lo || off > hi) s[r] = -INFINITY;
       }
     }
     float* xs = &sX[u & 1][pair][0];

@@ -73,13 +73,19 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// K tile rows are D bytes (D/16 chunks); XOR on the chunk index so that the
-// 8 rows {0..3, 16..19} (+4, +8, ...) read together hit distinct banks.
+// LDS banks: 64 of 4 bytes, a 16-byte access served 16 lanes (256 bytes) at
+// a time.  K tile rows are D bytes (D/16 chunks); the 16 lanes of an A-operand
+// read take rows {0..7} + {0, 16} (+8, +32) at one logical chunk, and rows
+// that share a 256-byte bank row (256 / D of them) must get distinct chunks:
+// the XOR takes the row bits above those (within 0..7) and bit 4.
 template <int D> __device__ __forceinline__ int swz_k8(int r) {
-  return D >= 128 ? ((r & 3) | (((r >> 4) & 1) << 2)) : (r & 3);
+  if constexpr (D == 64) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+  if constexpr (D == 128) return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+  return (r & 7) | (((r >> 4) & 1) << 3);
 }
-// V^T tile rows are 64 bytes (4 chunks).
-__device__ __forceinline__ int swz_v8(int d) { return (d >> 1) & 3; }
+// V^T tile rows are 64 bytes (4 chunks, four rows per bank row); a read takes
+// 16 consecutive rows at one logical chunk, so rows 4 apart get distinct chunks.
+__device__ __forceinline__ int swz_v8(int d) { return (d >> 2) & 3; }
 
 __device__ __forceinline__ i32x8 cat(u32x4 a, u32x4 b) {
   return (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2],
@@ -110,8 +116,10 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   __shared__ __attribute__((aligned(16))) uint8_t sV1[VTB];
 
   const int B = prm.B, Hq = prm.Hq, Hkv = prm.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index, wave-uniform (in an SGPR): so are the bounds derived from
+  // it, and the mask test of a tile is a scalar branch
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wu = w;
   const int l32 = lane & 31, hf = lane >> 5;
 
   const int nqt = (prm.Lq + kPBM - 1) / kPBM;
@@ -248,19 +256,24 @@ void fwd_fp8_kernel(const Fp8Params prm) {
         s[kb] = mfma_fp8(cat(a0, a1), qf[m], s[kb]);
       }
     }
-    // score element r of block kb is key j0 + 32kb + 16hf + r
-    const bool whole = j0 >= kmin(qw_last) && j0 + kPBN - 1 <= kmax(qw0);
+    // score element r of block kb is key j0 + 32kb + 16hf + r; a tile that
+    // some row of the wave does not see whole is masked (a scalar branch,
+    // then a select per element)
+    if (j0 < kmin(qw_last) || j0 + kPBN - 1 > kmax(qw0)) {
+      const int lo = row_kmin - j0 - 16 * hf, hi = row_kmax - j0 - 16 * hf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + r;
+          if (off < lo || off > hi) s[kb][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (!whole) {
-          const int key = j0 + 32 * kb + 16 * hf + r;
-          if (key < row_kmin || key > row_kmax) s[kb][r] = -INFINITY;
-        }
-        mx = fmaxf(mx, s[kb][r]);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = max_halves(mx);
     const bool upd = mx > m_ref + thr;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(upd) != 0, 0)) {
