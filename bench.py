@@ -110,9 +110,15 @@ def parse():
     return p.parse_args()
 
 
+# headers every kernel includes (helpers, work map, LDS layouts): part of every digest
+SHARED_HEADERS = ["fa_common.hpp", "fa_sched.hpp", "fa_lds.hpp"]
+
+
 def source_digest(names) -> str:
+    """Hash of a kernel's sources (the named files plus the shared headers),
+    tying a counter record to the code it was taken on."""
     h = hashlib.sha256()
-    for n in names:
+    for n in list(names) + [x for x in SHARED_HEADERS if x not in names]:
         with open(os.path.join(CSRC, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -76,21 +76,6 @@ struct BwdParams {
   int xcd_wq, xcd_wk;  // work-list windows of the dq and dkdv grids (xcd_work_item)
 };
 
-// XOR on a row's 16-byte chunk index in the LDS tiles.  Each tile is read two
-// ways: by rows (16 lanes, 256 bytes, read one logical chunk of 16 consecutive
-// rows) and by transpose reads (32 lanes, 256 bytes, read logical chunks
-// 4m .. 4m+3 of 4 consecutive rows, 8 bytes each).  At D >= 128 a row spans
-// all 64 banks, so the 16 rows need 16 distinct XOR values, and the 4 rows'
-// values must differ above bit 1 so that their chunk quads are disjoint: the
-// value swaps the two 2-bit halves of the row's low four bits.  At D = 64 two
-// rows share the banks (odd rows on the upper half), so the value is a
-// permutation of r >> 1 whose bit 2 separates rows 2 apart.
-template <int D> __device__ __forceinline__ int swz_b(int r) {
-  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  const int x = (r >> 1) & 7;
-  return ((x & 1) << 2) | (x >> 1);
-}
-
 // Rows of sequence b: queries qs .. qs+Lq-1 and keys ks .. ks+Lk-1.  Packed
 // offsets are clamped into the tensors and the lengths to the longest ones
 // the grid and the workspace are sized for, so that inconsistent offsets give

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_lds.hpp"
 #include "fa_sched.hpp"
 
 namespace fa {

@@ -55,25 +55,6 @@ static_assert(kKS == 16, "the decode MFMA layout assumes 16-key steps");
 
 constexpr int kDW = 4;  // waves per split workgroup
 
-// LDS bank layout (64 banks of 4 bytes; an access is served 256 bytes at a
-// time: 16 lanes of a 16-byte access, 32 of an 8-byte one).
-//
-// XOR on the 16-byte chunk index of row r of a tile whose rows hold N chunks,
-// read 16 consecutive rows at one logical chunk: rows sharing a 256-byte bank
-// row (16 / N of them when N < 16) get distinct chunks.
-template <int N> __device__ __forceinline__ int row_xor(int r) {
-  return N >= 16 ? (r & 15) : ((r / (16 / N)) & (N - 1));
-}
-
-// XOR on the 16-byte chunk index of row r of a V tile.  A transpose read of 32
-// lanes touches chunks 2m, 2m+1 of 8 consecutive rows, so bits above 0 spread
-// the rows' chunk pairs; bit 0 alternates between the rows a 16-lane store of
-// widened int8 codes covers together (its first store writes chunk 2c of each
-// row), so those rows land on even and odd chunks.
-template <int D> __device__ __forceinline__ int swz_dv(int r) {
-  return D == 64 ? (2 * ((r >> 1) & 3) | ((r >> 1) & 1)) : (2 * (r & 7) | (r & 1));
-}
-
 struct SplitParams {
   const uint16_t* Q;
   const void* K;  // dense [B, Lmax, Hkv, D]; paged [num_pages, P, Hkv, D]; 16-bit or int8

@@ -73,20 +73,6 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// LDS banks: 64 of 4 bytes, a 16-byte access served 16 lanes (256 bytes) at
-// a time.  K tile rows are D bytes (D/16 chunks); the 16 lanes of an A-operand
-// read take rows {0..7} + {0, 16} (+8, +32) at one logical chunk, and rows
-// that share a 256-byte bank row (256 / D of them) must get distinct chunks:
-// the XOR takes the row bits above those (within 0..7) and bit 4.
-template <int D> __device__ __forceinline__ int swz_k8(int r) {
-  if constexpr (D == 64) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
-  if constexpr (D == 128) return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
-  return (r & 7) | (((r >> 4) & 1) << 3);
-}
-// V^T tile rows are 64 bytes (4 chunks, four rows per bank row); a read takes
-// 16 consecutive rows at one logical chunk, so rows 4 apart get distinct chunks.
-__device__ __forceinline__ int swz_v8(int d) { return (d >> 2) & 3; }
-
 __device__ __forceinline__ i32x8 cat(u32x4 a, u32x4 b) {
   return (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2],
                  (int)b[3]};
