@@ -16,8 +16,8 @@
 //     row 8g + 4h + i, so each lane's 16 scores of a block are 16 consecutive
 //     keys (16h .. 16h+15 of the block).
 //   * O^T += V^T P^T: one MFMA (k = 64 keys) per 32 head dimensions.  B =
-//     P^T straight from the score registers, scaled by 256 (so the e4m3
-//     rounding stays clear of subnormals; the factor is added as 8 to the
+//     P^T straight from the score registers, scaled by 2^kPExp (so that the
+//     e4m3 rounding stays clear of subnormals; the factor is added to the
 //     exponent and removed through the row sum) and packed with
 //     v_cvt_pk_fp8_f32;
 //     A = 32 bytes of one V^T row (two ds_read_b128 of keys 16h.. and
@@ -25,8 +25,8 @@
 //     operands of the f8f6f4 MFMA share their k layout, so matching byte
 //     positions is all that is needed.
 //   * Online softmax as in the 16-bit forward, with the lazy rescale limited
-//     to a factor of 2^0.5 so that 256 * P stays below e4m3's 448.  The row sum
-//     adds the unrounded fp32 probabilities.
+//     to a factor of 2^kSlack so that 2^kPExp * P stays below e4m3's 448.  The
+//     row sum adds the unrounded fp32 probabilities.
 //   * K and V^T tiles stream HBM -> LDS with LDS-direct copies, two stages.
 //   * O is staged through the tile arrays and written as whole rows with
 //     non-temporal stores.
@@ -49,6 +49,14 @@ constexpr int kPT = kPW * 64;     // threads
 constexpr int kPR = 32;           // query rows per wave
 constexpr int kPBM = kPW * kPR;   // query rows per workgroup
 constexpr int kPBN = 64;          // keys per tile
+// P enters the PV product as 2^kPExp * P in e4m3, and a row's maximum may grow
+// by kSlack (base-2 exponent units) past the reference the accumulators are
+// scaled to before they are rescaled: 2^(kPExp + kSlack) ~ 362 stays below
+// e4m3's largest finite value, 448, and every P down to 2^-(6 + kPExp) of the
+// reference is a normal e4m3 number.  Random scores of unit spread outgrow a
+// slack of 0.5 in about half the tiles of a 32-row wave, 2.5 in about one in
+// eight; each rescale is a multiply per accumulator.
+constexpr float kPExp = 6.f, kSlack = 2.5f;
 
 struct Fp8Params {
   const uint8_t* Q;
@@ -271,11 +279,11 @@ void fwd_fp8_kernel(const Fp8Params prm) {
       for (int i = 0; i < DV / 32; ++i) acc[i] *= alpha;
       m_ref = m_new;
     }
-    // 256 P (the factor keeps the e4m3 rounding clear of subnormals; it enters
-    // as +8 in the exponent and leaves through the row sum), packed four keys
+    // 2^kPExp P (the factor keeps the e4m3 rounding clear of subnormals; it
+    // enters the exponent and leaves through the row sum), packed four keys
     // per dword: dword j of the B operand carries keys 16(j/4)... i.e. block
     // j/4, elements 4(j%4)..+3.
-    const float mb = ((m_ref == -INFINITY) ? 0.f : m_ref * scale2) - 8.f;
+    const float mb = ((m_ref == -INFINITY) ? 0.f : m_ref * scale2) - kPExp;
     i32x8 pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -349,7 +357,7 @@ void fwd_fp8_kernel(const Fp8Params prm) {
   }
   if (split == 0 && hf == 0 && qrow < Lq)  // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
     __builtin_nontemporal_store(
-        l > 0.f ? (m_ref * scale2 + __builtin_log2f(l) - 8.f) * kLn2 : -INFINITY,
+        l > 0.f ? (m_ref * scale2 + __builtin_log2f(l) - kPExp) * kLn2 : -INFINITY,
         prm.LSE + (prm.cu_q ? (long)h * prm.total_q + qs + qrow : ((long)b * Hq + h) * Lq + qrow));
 }
 
@@ -375,7 +383,7 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
   p.win_right = a.win_right;
   const float sc = a.scale * a.q_descale * a.k_descale;
   p.scale2 = fmaxf(fabsf(sc) * kLog2e, 1e-30f);
-  p.thr = 0.5f / p.scale2;
+  p.thr = kSlack / p.scale2;
   p.oscale = a.v_descale;
   p.qxor = sc < 0.f ? 0x80808080u : 0u;
   const int nqt = (a.Lq + kPBM - 1) / kPBM;

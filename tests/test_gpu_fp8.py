@@ -4,7 +4,7 @@ oracle on the decoded e4m3 inputs.
 Error bound (derived from the arithmetic): the scores of e4m3 codes are exact
 products summed in fp32, so the only rounding beyond the 16-bit output is P's
 rounding to e4m3 for the PV product (relative error <= 2^-4 for the normal
-range; 256 * P keeps P >= 2^-14 normal).  Hence per element
+range; 64 * P keeps P >= 2^-12 of the running reference normal).  Hence per element
 |dO| <= 2^-4 * sum_j P_ij |v_j| (the oracle's `mag`) + u_out |O| + 1e-4, and lse
 (from unrounded probabilities) keeps the 16-bit path's 1e-3 bound.
 """
