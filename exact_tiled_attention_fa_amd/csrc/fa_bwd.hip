@@ -14,8 +14,9 @@
 // Three kernels, none of them with atomics (results are bitwise
 // reproducible):
 //   * prep: D_i and lse_i * log2(e) per row into a workspace (+inf for rows
-//     that see no key and for the padding rows past a sequence's end, whose
-//     D is 0, so their probabilities and dS come out exactly 0).
+//     that see no key and for the padding rows past a sequence's end in its
+//     last 32-row tile, whose D is 0, so their probabilities and dS come out
+//     exactly 0).
 //   * dq (query-major, like the forward): a workgroup owns 128 query rows (32
 //     per wave, one per lane column) and streams K/V tiles of 32 keys through
 //     LDS (LDS-direct copies, two stages).  Per tile and wave:
@@ -64,7 +65,8 @@ struct BwdParams {
   uint16_t* dK;
   uint16_t* dV;
   float* lse2;  // workspace [B, Hq, Lqp]: lse * log2(e), +inf for rows with no key and padding rows
-  float* Dd;    // workspace [B, Hq, Lqp]: rowsum(dO * O), 0 for padding rows
+  float* Dd;    // workspace [B, Hq, Lqp]: rowsum(dO * O), 0 for padding rows (those of a
+                // sequence's last 32-row tile; the tiles past it are not written)
   const int* cu_q;  // packed sequences: offsets [B + 1] into the rows, or nullptr
   const int* cu_k;
   int total_q, total_k;  // packed row counts
@@ -93,46 +95,53 @@ __device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b) {
   return r;
 }
 
-// Per-row statistics: D_i = dO_i . O_i and lse_i * log2(e).  CPR lanes (one
-// 16-byte chunk each) per (row, head); rows in memory order [B, Lq, Hq].
-// The workspace rows past a sequence's end (up to the padded length Lqp) get
-// lse2 = +inf and D = 0, so that they give P = 0 and dS = 0 exactly.
+// Per-row statistics: D_i = dO_i . O_i and lse_i * log2(e).  A workgroup
+// takes 32 consecutive query rows of one (sequence, head), the workspace's own
+// order, so that each of its two stores is one whole 128-byte line; 8 lanes
+// share a row (D / 64 16-byte chunks each, whole rows per group of lanes).
+// The workspace rows past a sequence's end, up to the end of its last 32-row
+// query tile, get lse2 = +inf and D = 0, so that they give P = 0 and dS = 0
+// exactly.  Tiles past that (packed sequences shorter than the longest) are
+// read by neither later kernel and are left unwritten.
+constexpr int kPrepLanes = 8;                         // lanes per row
+constexpr int kPrepRows = 256 / kPrepLanes;           // rows per workgroup
+static_assert(kPrepRows == kTile, "one workgroup per 32-row query tile");
+
 template <typename T, int D>
 __global__ __launch_bounds__(256)
 void bwd_prep_kernel(const BwdParams p) {
-  constexpr int CPR = D / 8;
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gid / CPR;  // (b * Lqp + i) * Hq + h; packed: Lqp pads the longest length
-  const int c = (int)(gid % CPR);
-  const long nrows = (long)p.B * p.Lqp * p.Hq;
-  const int h = (int)(row % p.Hq);
-  const long bi = row / p.Hq;
-  const int i = (int)(bi % p.Lqp);
-  const int b = (int)(bi / p.Lqp);
-  const bool inrange = row < nrows;
-  bool valid = false;
-  SeqRows sr{0, 0, 0, 0};
-  if (inrange) {
-    sr = seq_rows(p, b);
-    valid = i < sr.Lq;
-  }
-  const long mrow = (long)(sr.qs + i) * p.Hq + h;  // row of O / dO in memory
+  constexpr int CPL = D / 8 / kPrepLanes;  // 16-byte chunks per lane
+  const int ntile = p.Lqp / kPrepRows;
+  const int tile = (int)(blockIdx.x % (unsigned)ntile);
+  const int bh = (int)(blockIdx.x / (unsigned)ntile);  // b * Hq + h
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const SeqRows sr = seq_rows(p, b);
+  const int i0 = tile * kPrepRows;
+  if (i0 >= (sr.Lq + kTile - 1) / kTile * kTile) return;  // whole workgroup
+  const int r = threadIdx.x / kPrepLanes, c = threadIdx.x % kPrepLanes;
+  const int i = i0 + r;
+  const bool valid = i < sr.Lq;
   float acc = 0.f;
   if (valid) {
-    // read once here: non-temporal (whole rows per group of CPR lanes)
-    const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.O + mrow * D + 8 * c));
-    const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.dO + mrow * D + 8 * c));
+    const long mrow = (long)(sr.qs + i) * p.Hq + h;  // row of O / dO in memory
+    // read once here: non-temporal
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc += Ops<T>::lo(o[e]) * Ops<T>::lo(g[e]) + Ops<T>::hi(o[e]) * Ops<T>::hi(g[e]);
+    for (int k = 0; k < CPL; ++k) {
+      const int off = 8 * (c + kPrepLanes * k);
+      const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.O + mrow * D + off));
+      const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.dO + mrow * D + off));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc += Ops<T>::lo(o[e]) * Ops<T>::lo(g[e]) + Ops<T>::hi(o[e]) * Ops<T>::hi(g[e]);
+    }
   }
 #pragma unroll
-  for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (inrange && c == 0) {
-    const long oi = ((long)b * p.Hq + h) * p.Lqp + i;
+  for (int m = kPrepLanes / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (c == 0) {
+    const long oi = (long)bh * p.Lqp + i;
     if (valid) {
       // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
-      const long li = p.cu_q ? (long)h * p.total_q + sr.qs + i : ((long)b * p.Hq + h) * p.Lq + i;
+      const long li = p.cu_q ? (long)h * p.total_q + sr.qs + i : (long)bh * p.Lq + i;
       const float l = p.LSE[li];
       p.Dd[oi] = acc;
       p.lse2[oi] = l == -INFINITY ? INFINITY : l * kLog2e;
@@ -738,10 +747,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.qxor = a.scale < 0.f ? 0x80008000u : 0u;
 
-  const long nrows = (long)a.B * p.Lqp * a.Hq;
-  const long nthreads = nrows * (D / 8);
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((long)a.B * a.Hq * (p.Lqp / kPrepRows))),
+                     dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqt = (a.Lq + kBM - 1) / kBM;
