@@ -421,7 +421,8 @@ const char* fa_last_error(void) { return g_err; }
 
 const char* fa_info(void) {
   return "arch=gfx950; head_dims={64,128,256}; dtypes={f16,bf16}; "
-         "fwd: 4 wave64 x 32 query rows per workgroup (BM=128), 32-key tiles, "
+         "fwd: 4 wave64 x 32 query rows per workgroup (BM=128; at D=256 8 wave64, two per "
+         "row slice splitting the head dims), 32-key tiles, "
          "mfma_f32_32x32x16, LDS-direct K/V with transpose reads, causal/window tile "
          "skip, block-diagonal packing, GQA; "
          "bwd: dQ query-major, dK/dV key-major in pairs of waves, dense and packed, D={64,128,256}; "

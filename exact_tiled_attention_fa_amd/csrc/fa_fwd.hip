@@ -51,6 +51,16 @@
 //   * The output tile is staged through LDS so each row is written to HBM as
 //     full contiguous 16-byte-per-lane stores, non-temporal (O is not read
 //     back here).
+//   * At D = 256 one wave holding Q^T, the accumulator and two score tiles
+//     for all 256 dims needs more than 256 registers (one wave per SIMD).
+//     There a workgroup has 8 waves and two share each 32-row slice: wave w
+//     and w + 4 each hold half of the head dims (their Q^T, K and V^T columns
+//     and accumulator), form a partial S over that half and exchange it
+//     through LDS; both then hold the same full S, and so the same softmax
+//     (the sum is taken in the same order on both), and each forms P V for
+//     its own half.  S(t+1) is exchanged during step t and summed after the
+//     barrier that opens step t+1, so the exchange needs no barrier of its
+//     own.  No MFMA work is done twice.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -59,7 +69,10 @@
 namespace fa {
 namespace {
 
-constexpr int kNT = kFwdWaves * 64;
+// Waves per workgroup and head dims per wave (two waves share a row slice at
+// D = 256, each holding half of the dims).
+template <int D> constexpr bool fwd_split() { return D == 256; }
+template <int D> constexpr int fwd_waves() { return fwd_split<D>() ? 2 * kFwdWaves : kFwdWaves; }
 
 // Keys per KV tile.  The pipelined loop keeps two score tiles, the packed
 // probabilities, the output accumulator and Q in registers; at D >= 128 a
@@ -111,19 +124,24 @@ struct FwdParams {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kNT, (D <= 128 ? 2 : 1))
+__global__ __launch_bounds__(fwd_waves<D>() * 64, (D <= 128 ? 2 : 1))
 void fwd_kernel(const FwdParams prm) {
   const int B = prm.B, Hq = prm.Hq, Hkv = prm.Hkv;
   const float scale2 = prm.scale2;
   const uint32_t qxor = prm.qxor;
+  constexpr bool SPLIT = fwd_split<D>();
+  constexpr int NW = fwd_waves<D>();         // waves per workgroup
+  constexpr int NT = NW * 64;
+  constexpr int DH = SPLIT ? D / 2 : D;      // head dims per wave
   constexpr int BM = kFwdBM;
   constexpr int BN = FwdTile<D>::BN;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = BN * D;               // elements per K or V tile
-  constexpr int NLOAD = BN * CPR / kNT;      // LDS-direct loads per thread per tile (each of K, V)
-  static_assert(BN % 32 == 0 && D % 32 == 0 && (BN * CPR) % kNT == 0, "tile shape");
-  // The output is staged through LDS, one K/V tile array per wave.
-  static_assert(kFwdWaves == 4 && 32 * D <= TILE, "O stage");
+  constexpr int NLOAD = BN * CPR / NT;       // LDS-direct loads per thread per tile (each of K, V)
+  static_assert(BN % 32 == 0 && D % 32 == 0 && (BN * CPR) % NT == 0, "tile shape");
+  // The output is staged through LDS: each wave's 32 x DH block in a quarter
+  // (an eighth when split) of the four K/V tile arrays.
+  static_assert(kFwdWaves == 4 && NW * 32 * DH <= 4 * TILE, "O stage");
   // kStages stages of K and V tiles.  Distinct arrays (not slices of one)
   // let the compiler see that reading one stage does not alias the
   // LDS-direct copy into another, so it inserts no wait between them.
@@ -136,6 +154,9 @@ void fwd_kernel(const FwdParams prm) {
   __shared__ __attribute__((aligned(16))) uint16_t sV2[T2];
   __shared__ __attribute__((aligned(16))) uint16_t sK3[T2];
   __shared__ __attribute__((aligned(16))) uint16_t sV3[T2];
+  // Split waves: partial score tiles, two buffers x NW waves x BN/32 blocks
+  // of 1024 floats (lane-major float4s, conflict-free).
+  __shared__ __attribute__((aligned(16))) float sX[SPLIT ? 2 * NW * (BN / 32) * 1024 : 4];
   auto kst = [&](auto I) -> uint16_t* {
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return sK0; else if constexpr (i == 1) return sK1;
@@ -152,6 +173,8 @@ void fwd_kernel(const FwdParams prm) {
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
+  const int wr = SPLIT ? (w & (kFwdWaves - 1)) : w;  // 32-row slice
+  const int dh0 = SPLIT ? (w / kFwdWaves) * DH : 0;  // first head dim of this wave
 
   const int nqt = (prm.Lq + BM - 1) / BM;
   int b, h, qt;
@@ -173,7 +196,7 @@ void fwd_kernel(const FwdParams prm) {
   }
   const int q0 = qt * BM;
   if (q0 >= Lq) return;  // past this sequence's rows (whole workgroup)
-  const int qw0 = q0 + kFwdRowsPerWave * w;
+  const int qw0 = q0 + kFwdRowsPerWave * wr;
   const int qrow = qw0 + l32;
 
   // Keys row i may see: [kmin(i), kmax(i)], both non-decreasing in i.
@@ -201,7 +224,7 @@ void fwd_kernel(const FwdParams prm) {
   uint32_t ldk[NLOAD], ldv[NLOAD];
 #pragma unroll
   for (int i = 0; i < NLOAD; ++i) {
-    const int P = (i * kFwdWaves + wu) * 64 + lane;
+    const int P = (i * NW + wu) * 64 + lane;
     const int r = P / CPR, pc = P % CPR;
     ldk[i] = 2u * (uint32_t)(r * (int)kstride + 8 * (pc ^ swz_k<D>(r)));
     ldv[i] = 2u * (uint32_t)(r * (int)kstride + 8 * (pc ^ swz_v<D>(r)));
@@ -209,7 +232,7 @@ void fwd_kernel(const FwdParams prm) {
   // Rows past Lk (only in the last tile) are redirected to row Lk-1: any
   // finite row will do, their scores are masked.
   auto clamp_off = [&](int i, int j0, uint32_t off) {
-    const int r = ((i * kFwdWaves + wu) * 64 + lane) / CPR;
+    const int r = ((i * NW + wu) * 64 + lane) / CPR;
     return off - 2u * (uint32_t)(((j0 + r) - min(j0 + r, Lk - 1)) * (int)kstride);
   };
   auto issue = [&](const uint16_t* src, const uint32_t (&ld)[NLOAD], int t, uint16_t* dst) {
@@ -217,30 +240,31 @@ void fwd_kernel(const FwdParams prm) {
     const uint16_t* base = src + (long)j0 * kstride;  // wave-uniform
     if (j0 + BN <= Lk) {
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * kFwdWaves + wu) * 512);
+      for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * NW + wu) * 512);
     } else {
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i)
-        load_lds16_off(base, clamp_off(i, j0, ld[i]), dst + (i * kFwdWaves + wu) * 512);
+        load_lds16_off(base, clamp_off(i, j0, ld[i]), dst + (i * NW + wu) * 512);
     }
   };
   // Main-phase copies: the tile is whole and inside the sequence, no clamping;
   // `base` is a running wave-uniform pointer to the tile's first row.
   auto issue_whole = [&](const uint16_t* base, const uint32_t (&ld)[NLOAD], uint16_t* dst) {
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * kFwdWaves + wu) * 512);
+    for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * NW + wu) * 512);
   };
   const long tstride = (long)BN * kstride;
   const uint16_t* kp = Kb;
   const uint16_t* vp = Vb;
   auto issue_k = [&](int u, uint16_t* dK) { issue(Kb, ldk, t_first + u, dK); };
   auto issue_v = [&](int u, uint16_t* dV) { issue(Vb, ldv, t_first + u, dV); };
-  // Q^T operand: lane holds query `qrow`, 8 dims per 16-dim k-step.
-  u32x4 qf[D / 16];
+  // Q^T operand: lane holds query `qrow`, 8 dims per 16-dim k-step (of this
+  // wave's DH dims).
+  u32x4 qf[DH / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
+  for (int s = 0; s < DH / 16; ++s) {
     if (qrow < Lq) {
-      u32x4 x = load16(Qb + (long)qrow * qstride + 16 * s + 8 * hf);
+      u32x4 x = load16(Qb + (long)qrow * qstride + dh0 + 16 * s + 8 * hf);
       qf[s] = x ^ qxor;  // negative scales: flip the sign of q, use |scale|
     } else {
       qf[s] = (u32x4){0u, 0u, 0u, 0u};
@@ -248,16 +272,17 @@ void fwd_kernel(const FwdParams prm) {
   }
 
   // Per-lane LDS element offsets of the MFMA operand reads.
-  int koff[D / 16];
+  int koff[DH / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = l32 * D + 8 * ((2 * kk + hf) ^ swz_k<D>(l32));
+  for (int kk = 0; kk < DH / 16; ++kk)
+    koff[kk] = l32 * D + 8 * ((dh0 / 8 + 2 * kk + hf) ^ swz_k<D>(l32));
   // V^T read for k-step t, half r, head-dim block db: row 16t + 8r + 4hf + (lane%16)/4,
   // columns 32db + 16*((lane/16)%2) + 4*(lane%4) .. +3.  swz_v depends only on the lane here.
   const int vrow = 4 * hf + ((lane & 15) >> 2);
-  int voff[D / 32];
+  int voff[DH / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  for (int db = 0; db < DH / 32; ++db) {
+    const int col = dh0 + 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     voff[db] = vrow * D + 8 * ((col >> 3) ^ swz_v<D>(vrow)) + (col & 7);
   }
 
@@ -268,9 +293,9 @@ void fwd_kernel(const FwdParams prm) {
   const int first_live = wave_live ? kmin(qw0) / BN - t_first : ntiles;
   const int last_live = wave_live ? kmax(qw_last) / BN - t_first : -1;
 
-  f32x16 acc[D / 32];
+  f32x16 acc[DH / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  for (int i = 0; i < DH / 32; ++i) acc[i] = (f32x16){};
   float m_ref = -INFINITY;  // reference max (raw score units) of this lane's row
   float l_part = 0.f;       // this lane's half of the row sum (relative to m_ref)
 
@@ -281,7 +306,7 @@ void fwd_kernel(const FwdParams prm) {
     for (int kb = 0; kb < BN / 32; ++kb) {
       s[kb] = (f32x16){};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+      for (int kk = 0; kk < DH / 16; ++kk) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(sK + 32 * kb * D + koff[kk]);
         s[kb] = Ops<T>::mfma32(a, qf[kk], s[kb]);
       }
@@ -344,7 +369,7 @@ void fwd_kernel(const FwdParams prm) {
         const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast((m_ref - mx) * scale2);
         l_part *= alpha;
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        for (int i = 0; i < DH / 32; ++i) acc[i] *= alpha;
         m_ref = mx;
       }
       ls = exp_pack(s, pk);
@@ -358,13 +383,40 @@ void fwd_kernel(const FwdParams prm) {
       const int kb = ts >> 1, c = ts & 1;
       const u32x4 bop = {pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]};
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < DH / 32; ++db) {
         const u32x2 lo = lds_read_tr16(sV + 16 * ts * D + voff[db]);
         const u32x2 hi = lds_read_tr16(sV + (16 * ts + 8) * D + voff[db]);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         acc[db] = Ops<T>::mfma32(a, bop, acc[db]);
       }
     }
+  };
+
+  // Split waves: this wave's partial scores of a tile go to buffer X of the
+  // exchange; the partner's (the other half of the head dims) are added in
+  // after the next barrier.  The two sums are the same floating-point sum
+  // (addition commutes exactly), so both waves hold the same full scores.
+  auto xput = [&](const f32x16 (&s)[BN / 32], auto X) {
+    constexpr int x = decltype(X)::value;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(sX + ((x * NW + w) * (BN / 32) + kb) * 1024 + 4 * (64 * g + lane)) =
+            (f32x4){s[kb][4 * g], s[kb][4 * g + 1], s[kb][4 * g + 2], s[kb][4 * g + 3]};
+  };
+  auto xadd = [&](f32x16 (&s)[BN / 32], auto X) {
+    constexpr int x = decltype(X)::value;
+    const int other = w ^ kFwdWaves;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(
+            sX + ((x * NW + other) * (BN / 32) + kb) * 1024 + 4 * (64 * g + lane));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kb][4 * g + i] += o[i];
+      }
   };
 
   // Tile t's K and V live in stage t % kStages.  Requests run kStages-1
@@ -403,6 +455,27 @@ void fwd_kernel(const FwdParams prm) {
       issue_whole(vp, ldv, vst(Iprev{}));
       kp += tstride;
       vp += tstride;
+    }
+    if constexpr (SPLIT) {
+      // S(t+1) is this wave's half; S(t) becomes whole here (the partner's
+      // half was stored during step t-1) and is masked only now.
+      using Xc = std::integral_constant<int, i & 1>;
+      using Xn = std::integral_constant<int, (i + 1) & 1>;
+      if (TAIL && (t > last_live || t + 1 < first_live)) return;
+      if (TAIL && t + 1 == first_live) {
+        scores(sn, kst(Inext{}));
+        xput(sn, Xn{});
+        return;
+      }
+      uint32_t pk[BN / 32][8];
+      const bool next = !TAIL || t + 1 <= last_live;
+      if (next) scores(sn, kst(Inext{}));
+      xadd(sc, Xc{});
+      if (TAIL) mask(sc, t);
+      make_p(sc, pk);
+      if (next) xput(sn, Xn{});
+      pv(pk, vst(I));
+      return;
     }
     if (TAIL && (t > last_live || t + 1 < first_live)) return;  // tile t and t+1 hidden from this wave
     if (TAIL && t + 1 == first_live) {  // tile t hidden, t+1 the wave's first
@@ -446,7 +519,10 @@ void fwd_kernel(const FwdParams prm) {
     tile_wait_barrier(std::integral_constant<int, (kStages - 1) * kPerTile>{});  // K(0) landed
     if (first_live == 0 && last_live >= 0) {
       scores(sA, sK0);
-      mask(sA, 0);
+      if constexpr (SPLIT)
+        xput(sA, std::integral_constant<int, 0>{});  // summed and masked in step 0
+      else
+        mask(sA, 0);
     }
     // Head phase (masked tiles left of some row's window), main phase
     // (unmasked, running tile pointers), tail phase (masked or partly skipped).
@@ -462,34 +538,39 @@ void fwd_kernel(const FwdParams prm) {
   // written as whole rows; lse = ln2 * (m*scale2 + log2 l).
   const float l = sum_halves(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  constexpr int OSW = CPR < 16 ? CPR - 1 : 15;
+  constexpr int CPH = DH / 8;  // 16-byte chunks of this wave's part of a row
+  constexpr int OSW = CPH < 16 ? CPH - 1 : 15;
   {
     __syncthreads();  // all waves are done with the K/V tiles
-    uint16_t* so = (w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1;
+    uint16_t* so;
+    if constexpr (SPLIT)
+      so = ((w >> 1) == 0 ? sK0 : (w >> 1) == 1 ? sV0 : (w >> 1) == 2 ? sK1 : sV1) + (w & 1) * 32 * DH;
+    else
+      so = (w == 0) ? sK0 : (w == 1) ? sV0 : (w == 2) ? sK1 : sV1;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d = 32 * db + 8 * a4 + 4 * hf;
         u32x2 val = {Ops<T>::pack2(acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv),
                      Ops<T>::pack2(acc[db][4 * a4 + 2] * inv, acc[db][4 * a4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(so + l32 * D + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
+        *reinterpret_cast<u32x2*>(so + l32 * DH + 8 * ((d >> 3) ^ (l32 & OSW)) + (d & 7)) = val;
       }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 32 * CPR / 64; ++i) {
+    for (int i = 0; i < 32 * CPH / 64; ++i) {
       const int p = lane + 64 * i;
-      const int row = p / CPR, c = p % CPR;
+      const int row = p / CPH, c = p % CPH;
       const int q = qw0 + row;
       if (q < Lq)
         // non-temporal: O is written once and not read back here (whole
         // rows per instruction, so no line is written in pieces)
         __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x4*>(so + row * D + 8 * (c ^ (row & OSW))),
-            reinterpret_cast<u32x4*>(prm.O + ((long)qs + q) * qstride + (long)h * D + 8 * c));
+            *reinterpret_cast<const u32x4*>(so + row * DH + 8 * (c ^ (row & OSW))),
+            reinterpret_cast<u32x4*>(prm.O + ((long)qs + q) * qstride + (long)h * D + dh0 + 8 * c));
     }
   }
-  if (hf == 0 && qrow < Lq) {
+  if (hf == 0 && qrow < Lq && dh0 == 0) {
     // lse: dense [B, Hq, Lq]; packed [Hq, total_q]
     const long li = prm.cu_q ? (long)h * prm.total_q + qs + qrow : ((long)bh * Lq + qrow);
     __builtin_nontemporal_store(
@@ -519,7 +600,8 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   p.qxor = (s < 0.f) ? 0x80008000u : 0u;
   // blocks resident per CU at this kernel's register use: 3 (D=64), 2, 1 (D=256)
   p.xcd_w = xcd_window(a.B, a.Hq, a.Hkv, nqt, D == 64 ? 3 : D == 128 ? 2 : 1);
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)nblocks), dim3(kNT), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)nblocks), dim3(fwd_waves<D>() * 64),
+                     0, stream, p);
   return hipGetLastError();
 }
 
