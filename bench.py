@@ -23,7 +23,9 @@ The other prefill workloads are timed after the step loop, each launch with
 its own HIP event pair, and reported under ``configs``: the long-context GQA
 prefill, the D=256 prefill, the bidirectional encoder (cold: a 512 MiB buffer
 is written between launches, outside the timed region, so that its inputs
-are not served from the 256 MiB last-level cache) and the tiny case (µs).
+are not served from the 256 MiB last-level cache) and the tiny case (µs:
+HIP events around each call, host time to the launch included, and per launch
+of 200 calls replayed from one HIP graph, the GPU's own time).
 The paged / int8 decode, FP8 forward, backward and structured-mask workloads
 follow under their own keys.  None of them is part of ``value``.
 
@@ -480,9 +482,44 @@ def time_prefill_cfg(name, dev, reps=50, cold=False):
            "kernel": f"fwd_kernel<{str(cfg.dtype)[6:].replace('float16', 'f16')}, {cfg.D}, "
                      f"{str(cfg.causal).lower()}>"}
     if name == "tiny":
+        # "us": HIP events around each call from Python, so the host's time to
+        # reach the launch is inside; "us_graph": the same call captured
+        # GRAPH_LAUNCHES times in one HIP graph and replayed, per launch (the
+        # GPU's own time with back-to-back launches)
         res["us"] = {k_: round(v_ * 1e3, 2) for k_, v_ in st.items() if k_ != "n"}
+        res["us_graph"] = {k_: round(v_ * 1e3 / GRAPH_LAUNCHES, 2)
+                           for k_, v_ in graph_replay_ms(run, GRAPH_LAUNCHES, 20).items()
+                           if k_ != "n"}
+        res["graph_launches"] = GRAPH_LAUNCHES
     del q, k, v, o, lse
     return res
+
+
+GRAPH_LAUNCHES = 200
+
+
+def graph_replay_ms(run, launches, reps):
+    """ms_stats of `reps` replays of one HIP graph holding `launches` calls of
+    run() (captured on a side stream of default priority, after one eager
+    warm-up call there)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(launches):
+            run()
+    torch.cuda.synchronize()
+    graph.replay()  # first replay uploads the graph
+    torch.cuda.synchronize()
+    st = ms_stats(time_launches(graph.replay, reps))
+    del graph
+    return st
 
 
 def _timed_block(run, reps):
