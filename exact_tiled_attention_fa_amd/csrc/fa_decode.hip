@@ -425,15 +425,30 @@ void decode_combine_kernel(const float* __restrict__ Opart, const float* __restr
   const int d = threadIdx.x;
   const float* lp = Lpart + bh * S;
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float l8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l8[i] = s0 + i < S ? lp[s0 + i] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, l8[i]);
+  }
   float out = 0.f, tot = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = lp[s];
-      if (ls == -INFINITY) continue;
-      const float wgt = exp2_fast(ls - M);
-      tot += wgt;
-      out += wgt * __builtin_nontemporal_load(Opart + (bh * S + s) * D + d);
+    // four partials requested at a time (their loads overlap); an empty
+    // chunk's partial was never written and is selected away, not weighted
+    const float* op = Opart + bh * S * D + d;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = s0 + i < S ? __builtin_nontemporal_load(op + (s0 + i) * D) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ls = s0 + i < S ? lp[s0 + i] : -INFINITY;
+        const float wgt = ls == -INFINITY ? 0.f : exp2_fast(ls - M);
+        tot += wgt;
+        out += ls == -INFINITY ? 0.f : wgt * o[i];
+      }
     }
     out /= tot;
   }
