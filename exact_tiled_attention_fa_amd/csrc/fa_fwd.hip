@@ -56,9 +56,9 @@
 //     There a workgroup has 8 waves and two share each 32-row slice: wave w
 //     and w + 4 each hold half of the head dims (their Q^T, K and V^T columns
 //     and accumulator), form a partial S over that half and exchange it
-//     through LDS; both then hold the same full S, and so the same softmax
-//     (the sum is taken in the same order on both), and each forms P V for
-//     its own half.  S(t+1) is exchanged during step t and summed after the
+//     through LDS; both then hold the same full S (own half + other half is
+//     the same floating-point sum on both sides, addition commuting exactly),
+//     so the same softmax, and each forms P V for its own half.  S(t+1) is exchanged during step t and summed after the
 //     barrier that opens step t+1, so the exchange needs no barrier of its
 //     own.  No MFMA work is done twice.
 #include <type_traits>
