@@ -7,7 +7,11 @@
 //     the main phase issues without clamping lies whole inside the keys,
 //     every tile the main phase computes unmasked is seen whole by every row
 //     of the workgroup, and each wave forms S and P.V exactly once for each
-//     tile holding keys its rows see, and for no other.
+//     tile holding keys its rows see, and for no other;
+//   * the score exchange of the split waves (D = 256, two waves per row
+//     slice, partial scores through a two-buffer LDS exchange): every tile
+//     whose scores a wave completes was stored in the buffer of its parity
+//     during the step just before (or the prologue) and not overwritten.
 // Prints one line per failure and exits non-zero if there is any.
 #include <cstdio>
 #include <cstdlib>
@@ -68,6 +72,9 @@ void check_walk(int Lq, int Lk, bool causal, int wl, int wr, int BN) {
     // per wave: the tiles holding keys its rows see, and how often S and PV ran
     int first_live[kWaves], last_live[kWaves];
     std::vector<int> s_cnt[kWaves], p_cnt[kWaves];
+    // split waves: the tile and the step (-1: prologue) of each exchange
+    // buffer's last store
+    int buf_tile[kWaves][2], buf_step[kWaves][2];
     for (int w = 0; w < kWaves; ++w) {
       const int qw0 = q0 + kRows * w, qwl = fa::imin(qw0 + kRows - 1, Lq - 1);
       const bool live = qw0 < Lq && kr.kmax(qwl) >= kr.kmin(qw0);
@@ -75,7 +82,11 @@ void check_walk(int Lq, int Lk, bool causal, int wl, int wr, int BN) {
       last_live[w] = live ? kr.kmax(qwl) / BN - walk.t_first : -1;
       s_cnt[w].assign(nt + 1, 0);
       p_cnt[w].assign(nt + 1, 0);
-      if (first_live[w] == 0 && last_live[w] >= 0) s_cnt[w][0]++;  // prologue
+      for (int x = 0; x < 2; ++x) buf_tile[w][x] = buf_step[w][x] = -100;
+      if (first_live[w] == 0 && last_live[w] >= 0) {  // prologue
+        s_cnt[w][0]++;
+        buf_tile[w][0] = 0, buf_step[w][0] = -1;
+      }
     }
     char tag[160];
     std::snprintf(tag, sizeof tag, "walk Lq=%d Lk=%d causal=%d win=(%d,%d) BN=%d q0=%d", Lq, Lk,
@@ -99,12 +110,25 @@ void check_walk(int Lq, int Lk, bool causal, int wl, int wr, int BN) {
               tag, t, t, t + 1);
       }
       for (int w = 0; w < kWaves; ++w) {
+        auto store = [&](int tile) {  // split: partial of `tile` into its parity's buffer
+          buf_tile[w][tile & 1] = tile, buf_step[w][tile & 1] = t;
+        };
         if (TAIL && (t > last_live[w] || t + 1 < first_live[w])) continue;
         if (TAIL && t + 1 == first_live[w]) {
           s_cnt[w][t + 1]++;
+          store(t + 1);
           continue;
         }
-        if (!TAIL || t + 1 <= last_live[w]) s_cnt[w][t + 1]++;
+        const bool next = !TAIL || t + 1 <= last_live[w];
+        // (waves whose rows all lie past the sequence run the main phase on
+        // whatever the buffer holds; their rows are never stored)
+        CHECK(q0 + kRows * w >= Lq || (buf_tile[w][t & 1] == t && buf_step[w][t & 1] == t - 1),
+              "%s wave %d: split scores of tile %d completed at step %d from a buffer holding "
+              "tile %d stored at step %d", tag, w, t, t, buf_tile[w][t & 1], buf_step[w][t & 1]);
+        if (next) {
+          s_cnt[w][t + 1]++;
+          store(t + 1);
+        }
         p_cnt[w][t]++;
       }
     };

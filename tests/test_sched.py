@@ -2,7 +2,9 @@
 compiles the same header the kernels use (csrc/fa_sched.hpp) with g++ and
 checks that every workgroup grid maps one-to-one onto its work items and that
 the prefill kernel's tile walk copies only whole in-range tiles without
-clamping and forms each visible tile exactly once per wave."""
+clamping and forms each visible tile exactly once per wave, and that the
+split waves' score exchange (D = 256) always completes a tile's scores from
+the partial stored for that tile in the step before."""
 
 from __future__ import annotations
 
