@@ -94,7 +94,7 @@ template <typename T> __device__ __forceinline__ u32x4 widen8(u32x2 x) {
 }
 
 template <typename T, int D, bool PAGED, bool KI8, bool VI8>
-__global__ __launch_bounds__(64 * kDW)
+__global__ __launch_bounds__(64 * kDW, (KI8 && VI8 && D <= 128) ? 3 : 1)
 void decode_split_kernel(const SplitParams prm) {
   const int Hq = prm.Hq, Hkv = prm.Hkv, Lmax = prm.Lmax, S = prm.S;
   const float scale2 = prm.scale2, thr = prm.thr;
@@ -355,23 +355,32 @@ void decode_split_kernel(const SplitParams prm) {
   };
 
   // Two-deep pipeline: the next step's K and V rows are requested before this
-  // step computes.  The request is unconditional (past the last step it
-  // re-reads the chunk's final row, a cache hit) so that the number of loads
-  // in flight, and thus each wait, is the same on every path.
+  // step computes.  In the loop the request is unconditional, so that the
+  // number of loads in flight, and thus each wait, is the same on every path;
+  // the last one or two steps are peeled off, so that no request reaches past
+  // the wave's last step (the merge below would wait for it).
   StepRegs rA, rB;
   load_step(w, rA);  // (a wave with no step reads the chunk's last step, unused)
   // The scheduling barriers keep each request ahead of the wait for the step
   // being computed, so two steps are in flight while that wait lasts.  (A
   // third step in flight, or 32-key steps for int8 caches, cost a wave per
   // SIMD in registers or serialise each wave further, and measured slower.)
-  for (int i = 0; i < my_steps; i += 2) {
+  int i = 0;
+  for (; i + 2 < my_steps; i += 2) {
     load_step(w + kDW * (i + 1), rB);
     __builtin_amdgcn_sched_barrier(0);
     compute(w + kDW * i, rA);
-    if (i + 1 >= my_steps) break;
     load_step(w + kDW * (i + 2), rA);
     __builtin_amdgcn_sched_barrier(0);
     compute(w + kDW * (i + 1), rB);
+  }
+  if (i + 1 < my_steps) {  // two steps left
+    load_step(w + kDW * (i + 1), rB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w + kDW * i, rA);
+    compute(w + kDW * (i + 1), rB);
+  } else if (i < my_steps) {  // one step left
+    compute(w + kDW * i, rA);
   }
 
   // Merge the waves: full row sums, per-wave normalised output and lse2 to LDS.
