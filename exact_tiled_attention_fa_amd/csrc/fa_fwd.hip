@@ -420,9 +420,10 @@ void fwd_kernel(const FwdParams prm) {
   };
 
   // Tile t's K and V live in stage t % kStages.  Requests run kStages-1
-  // tiles ahead (K one tile further, since S(t+1) is computed during step t)
-  // and are always issued -- past the last tile they re-read it -- so the
-  // number of copies in flight, and the wait below, is the same every step.
+  // tiles ahead (K one tile further, since S(t+1) is computed during step t).
+  // With more than two stages they are always issued -- past the last tile
+  // they re-read it -- so that the number of copies in flight, and the wait
+  // below, is the same every step; with two the wait takes every copy.
   constexpr int kPerTile = 2 * NLOAD;  // copies per thread per step (K and V)
   auto tile_wait_barrier = [&](auto young_tag) {
     // This wave's copies older than the `young` most recent have landed and
@@ -448,8 +449,11 @@ void fwd_kernel(const FwdParams prm) {
     using Iprev = std::integral_constant<int, (i + kStages - 1) % kStages>;
     tile_wait_barrier(std::integral_constant<int, (kStages - 2) * kPerTile>{});
     if (TAIL) {
-      issue_k(clampt(t + kStages), kst(I));
-      issue_v(clampt(t + kStages - 1), vst(Iprev{}));
+      // With two stages every step waits for all copies, so the copies past
+      // the last tile (re-reads, which the epilogue would wait for) can be
+      // left out; with more stages the wait counts need them.
+      if (kStages > 2 || t + kStages < ntiles) issue_k(clampt(t + kStages), kst(I));
+      if (kStages > 2 || t + kStages - 1 < ntiles) issue_v(clampt(t + kStages - 1), vst(Iprev{}));
     } else {
       issue_whole(kp, ldk, kst(I));
       issue_whole(vp, ldv, vst(Iprev{}));
