@@ -93,6 +93,9 @@ template <typename T> __device__ __forceinline__ u32x4 widen8(u32x2 x) {
   return r;
 }
 
+// The int8 keys-and-values instance at D <= 128 is held to 168 registers,
+// three waves per SIMD: it fits there, and each step of it moves half the bytes
+// of a 16-bit step, so it needs the extra wave's loads in flight.
 template <typename T, int D, bool PAGED, bool KI8, bool VI8>
 __global__ __launch_bounds__(64 * kDW, (KI8 && VI8 && D <= 128) ? 3 : 1)
 void decode_split_kernel(const SplitParams prm) {
