@@ -396,6 +396,8 @@ void fwd_kernel(const FwdParams prm) {
   // exchange; the partner's (the other half of the head dims) are added in
   // after the next barrier.  The two sums are the same floating-point sum
   // (addition commutes exactly), so both waves hold the same full scores.
+  // (A pair whose rows all lie past the sequence runs main-phase steps on
+  // whatever the buffer holds; its rows are never stored.)
   auto xput = [&](const f32x16 (&s)[BN / 32], auto X) {
     constexpr int x = decltype(X)::value;
 #pragma unroll
