@@ -103,6 +103,18 @@ __device__ __forceinline__ void load_lds16_off(const void* base, uint32_t off_by
   load_lds16(static_cast<const char*>(base) + off_bytes, lds);
 }
 
+// The same copy issued through the buffer path (buffer_load_dwordx4 ... lds)
+// from a wave-uniform base.  The compiler treats the global form as an access
+// that may touch LDS through FLAT, so while one is in flight every wait for an
+// LDS operand read drains all of them (lgkmcnt(0)); with the buffer form the
+// copy counts on vmcnt alone and reads issued ahead keep exact partial waits.
+// Descriptor: base, no stride, no range limit, 32-bit data format.
+__device__ __forceinline__ void load_lds16_buf(const void* base, uint32_t off_bytes, void* lds) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FA_LDS(void, lds), 16, off_bytes, 0, 0, 0);
+}
+
 // Wait until this wave's vector-memory loads (including LDS-direct ones) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
 

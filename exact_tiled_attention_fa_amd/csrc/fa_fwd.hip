@@ -90,6 +90,11 @@ template <int D> constexpr int fwd_waves() { return fwd_split<D>() ? 2 * kFwdWav
 // K/V tiles in flight: tile t+NS-1 (and K one further) is requested while
 // tile t is computed, which covers the HBM/L2 latency of the copies.
 constexpr int kStages = FA_FWD_STAGES;
+#ifndef FA_FWD_PF
+#define FA_FWD_PF 2
+#endif
+// LDS operand reads issued this many MFMAs ahead of their use.
+constexpr int kPF = FA_FWD_PF;
 static_assert(kStages == 2 || kStages == 4, "stage count");
 
 template <int D> struct FwdTile { static constexpr int BN = FA_FWD_BN_D64; };
@@ -240,18 +245,18 @@ void fwd_kernel(const FwdParams prm) {
     const uint16_t* base = src + (long)j0 * kstride;  // wave-uniform
     if (j0 + BN <= Lk) {
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * NW + wu) * 512);
+      for (int i = 0; i < NLOAD; ++i) load_lds16_buf(base, ld[i], dst + (i * NW + wu) * 512);
     } else {
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i)
-        load_lds16_off(base, clamp_off(i, j0, ld[i]), dst + (i * NW + wu) * 512);
+        load_lds16_buf(base, clamp_off(i, j0, ld[i]), dst + (i * NW + wu) * 512);
     }
   };
   // Main-phase copies: the tile is whole and inside the sequence, no clamping;
   // `base` is a running wave-uniform pointer to the tile's first row.
   auto issue_whole = [&](const uint16_t* base, const uint32_t (&ld)[NLOAD], uint16_t* dst) {
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) load_lds16_off(base, ld[i], dst + (i * NW + wu) * 512);
+    for (int i = 0; i < NLOAD; ++i) load_lds16_buf(base, ld[i], dst + (i * NW + wu) * 512);
   };
   const long tstride = (long)BN * kstride;
   const uint16_t* kp = Kb;
@@ -354,8 +359,7 @@ void fwd_kernel(const FwdParams prm) {
   // more than a few units above the reference, the first visible tile, or a
   // NaN) the tile's row max is folded in, the accumulator rescaled and the
   // probabilities recomputed.
-  auto make_p = [&](const f32x16 (&s)[BN / 32], uint32_t (&pk)[BN / 32][8]) {
-    float ls = exp_pack(s, pk);
+  auto accept = [&](float ls, const f32x16 (&s)[BN / 32], uint32_t (&pk)[BN / 32][8]) {
     const bool bad = !(ls <= 256.f) || m_ref == -INFINITY;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
       asm volatile("" ::: "memory");
@@ -376,8 +380,77 @@ void fwd_kernel(const FwdParams prm) {
     }
     l_part += ls;
   };
+  auto make_p = [&](const f32x16 (&s)[BN / 32], uint32_t (&pk)[BN / 32][8]) {
+    accept(exp_pack(s, pk), s, pk);
+  };
+  // S^T(t+1) = K Q^T fused with the first formation of P(t) from the scores
+  // sc: each MFMA is followed by its share of the exponentials, and the K
+  // operand of the MFMA kPF places later is read from LDS before it, so the
+  // reads' latency is covered by the MFMAs in between.  The scheduling fences
+  // keep the compiler from moving each read down to its use.  Returns this
+  // lane's sum of the probabilities (as exp_pack).
+  auto scores_exp = [&](f32x16 (&s)[BN / 32], const uint16_t* sK, const f32x16 (&sc)[BN / 32],
+                        uint32_t (&pk)[BN / 32][8]) {
+    constexpr int NK = DH / 16;            // MFMAs per 32-key block
+    constexpr int NM = (BN / 32) * NK;     // MFMAs of the tile
+    constexpr int NPAIR = (BN / 32) * 8;   // score pairs per lane
+    static_assert(NPAIR % NM == 0, "exponentials per MFMA");
+    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * scale2;
+    auto kread = [&](int i) {
+      return *reinterpret_cast<const u32x4*>(sK + 32 * (i / NK) * D + koff[i % NK]);
+    };
+    float ls = 0.f;
+    u32x4 a[NM];
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) a[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + kPF < NM) a[i + kPF] = kread(i + kPF);
+      const int kb = i / NK, kk = i % NK;
+      s[kb] = Ops<T>::mfma32(a[i], qf[kk], kk == 0 ? (f32x16){} : s[kb]);
+#pragma unroll
+      for (int jp = i * (NPAIR / NM); jp < (i + 1) * (NPAIR / NM); ++jp) {
+        const int kc = jp / 8, j = jp % 8;
+        const float p0 = exp2_fast(__builtin_fmaf(sc[kc][2 * j], scale2, -mb));
+        const float p1 = exp2_fast(__builtin_fmaf(sc[kc][2 * j + 1], scale2, -mb));
+        pk[kc][j] = Ops<T>::pack2(p0, p1);
+        ls += p0 + p1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return ls;
+  };
   // O^T += V^T P^T, 16 keys per MFMA k-step (slots 4r+k <-> key 16t+8r+4hf+k).
+  // The V^T operand of the MFMA kPF places later is read before each MFMA
+  // (fenced as in scores_exp).
   auto pv = [&](const uint32_t (&pk)[BN / 32][8], const uint16_t* sV) {
+    constexpr int NDB = DH / 32;
+    constexpr int NM = (BN / 16) * NDB;
+    auto vread = [&](int i) {
+      const int ts = i / NDB, db = i % NDB;
+      const u32x2 lo = lds_read_tr16(sV + 16 * ts * D + voff[db]);
+      const u32x2 hi = lds_read_tr16(sV + (16 * ts + 8) * D + voff[db]);
+      return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 a[NM];
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) a[i] = vread(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + kPF < NM) a[i + kPF] = vread(i + kPF);
+      const int ts = i / NDB, db = i % NDB;
+      const int kb = ts >> 1, c = ts & 1;
+      const u32x4 bop = {pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]};
+      acc[db] = Ops<T>::mfma32(a[i], bop, acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The same product with the reads left to the compiler's order (the split
+  // waves at D = 256, whose registers leave no room for reads ahead).
+  auto pv_plain = [&](const uint32_t (&pk)[BN / 32][8], const uint16_t* sV) {
 #pragma unroll
     for (int ts = 0; ts < BN / 16; ++ts) {
       const int kb = ts >> 1, c = ts & 1;
@@ -480,7 +553,7 @@ void fwd_kernel(const FwdParams prm) {
       if (TAIL) mask(sc, t);
       make_p(sc, pk);
       if (next) xput(sn, Xn{});
-      pv(pk, vst(I));
+      pv_plain(pk, vst(I));
       return;
     }
     if (TAIL && (t > last_live || t + 1 < first_live)) return;  // tile t and t+1 hidden from this wave
@@ -491,8 +564,7 @@ void fwd_kernel(const FwdParams prm) {
     }
     uint32_t pk[BN / 32][8];
     if (!TAIL || t + 1 <= last_live) {
-      scores(sn, kst(Inext{}));
-      make_p(sc, pk);
+      accept(scores_exp(sn, kst(Inext{}), sc, pk), sc, pk);
       pv(pk, vst(I));
       if (TAIL) mask(sn, t + 1);
     } else {
