@@ -180,7 +180,7 @@ struct TileLoader {
     for (int i = 0; i < NLOAD; ++i) {
       uint32_t o = off[i];
       if (!whole) o -= 2u * (uint32_t)(((r0 + rr[i]) - min(r0 + rr[i], last)) * stride);
-      load_lds16_off(base, o, dst + (i * kBW + wu) * 512);
+      load_lds16_buf(base, o, dst + (i * kBW + wu) * 512);
     }
   }
 };
@@ -441,7 +441,7 @@ struct PairTileLoader {
       const bool isg = c0 >= QCH;
       uint32_t o = off[i];
       if (!whole) o -= 2u * (uint32_t)(((r0 + rr[i]) - min(r0 + rr[i], last)) * stride);
-      load_lds16_off((isg ? g : q) + rb, o, (isg ? dg : dq) + (isg ? c0 - QCH : c0) * 8);
+      load_lds16_buf((isg ? g : q) + rb, o, (isg ? dg : dq) + (isg ? c0 - QCH : c0) * 8);
     }
   }
 };
@@ -560,16 +560,17 @@ void bwd_dkdv_kernel(const BwdParams p) {
   int toff[D / 32][2];
   tr_offsets<D>(lane, toff);
 
-  // lse2 / D copy: wave 0, lanes 0..15 (8 chunks of 4 rows each).
+  // lse2 / D copy: lanes 0..7 of waves 0 and 1 (8 chunks of 4 rows each).
   auto issue_tile = [&](int hg, int st, uint16_t* dq_tile, uint16_t* dg_tile, float* dl) __attribute__((always_inline)) {
     const int hh = kvh * g + hg;
     const int q0 = (s_first + st) * BQ;
     const long hbase = (long)sr.qs * qstride + (long)hh * D;
     ldr.issue(p.Q + hbase, p.dO + hbase, q0, Lq - 1, qstride, wu, dq_tile, dg_tile);
-    if (wu == 0 && lane < 16) {
+    if (wu < 2 && lane < 8) {
+      // wave 0 copies the 32 rows' lse2 to dl[0..31], wave 1 their D to
+      // dl[32..63] (one wave-uniform base each)
       const long sb = ((long)b * Hq + hh) * p.Lqp + q0;  // rows q0..q0+31 < Lqp
-      const float* src = (lane < 8 ? p.lse2 : p.Dd) + sb + 4 * (lane & 7);
-      load_lds16(src, dl);
+      load_lds16_buf(uniform_ptr((wu == 0 ? p.lse2 : p.Dd) + sb), 16u * lane, dl + 32 * wu);
     }
   };
 

@@ -108,11 +108,21 @@ __device__ __forceinline__ void load_lds16_off(const void* base, uint32_t off_by
 // that may touch LDS through FLAT, so while one is in flight every wait for an
 // LDS operand read drains all of them (lgkmcnt(0)); with the buffer form the
 // copy counts on vmcnt alone and reads issued ahead keep exact partial waits.
-// Descriptor: base, no stride, no range limit, 32-bit data format.
+// Descriptor: base, no stride, no range limit, 32-bit data format.  A base
+// the compiler cannot prove wave-uniform makes it loop over the base's
+// distinct values, so callers pass bases computed from uniform values only.
 __device__ __forceinline__ void load_lds16_buf(const void* base, uint32_t off_bytes, void* lds) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FA_LDS(void, lds), 16, off_bytes, 0, 0, 0);
+}
+
+// A pointer the caller knows to be wave-uniform, taken from the first active
+// lane so that the compiler holds it in scalar registers.
+template <typename P> __device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  return reinterpret_cast<P*>((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                              ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32));
 }
 
 // Wait until this wave's vector-memory loads (including LDS-direct ones) are done.

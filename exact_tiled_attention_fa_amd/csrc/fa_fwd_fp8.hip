@@ -216,12 +216,12 @@ void fwd_fp8_kernel(const Fp8Params prm) {
     for (int i = 0; i < NK; ++i) {
       uint32_t o = koff[i];
       if (!whole) o -= (uint32_t)(((j0 + krow[i]) - min(j0 + krow[i], LkA - 1)) * kstride);
-      load_lds16_off(kbase, o, dK + (i * kPW + wu) * 1024);
+      load_lds16_buf(kbase, o, dK + (i * kPW + wu) * 1024);
     }
     // V^T columns j0 .. j0+63 lie inside the row: dense, the stride is a
     // multiple of 64 >= Lk; packed, it is >= total_k + 64 and j0 <= dlt + Lk - 1
 #pragma unroll
-    for (int i = 0; i < NV; ++i) load_lds16_off(Vb + j0, voff[i], dV + (i * kPW + wu) * 1024);
+    for (int i = 0; i < NV; ++i) load_lds16_buf(Vb + j0, voff[i], dV + (i * kPW + wu) * 1024);
     kbase += ktile;
   };
 
