@@ -86,28 +86,19 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 #define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 #define FA_GLOBAL(T, p) ((__attribute__((address_space(1))) T*)(p))
 
-// Asynchronous 16-byte HBM -> LDS copy (global_load_lds_dwordx4).  `lds` must
-// be the same for every lane of the wave: lane l's 16 bytes land at lds + 16*l.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(FA_GLOBAL(void, g), FA_LDS(void, lds), 16, 0, 0);
-}
-
 // s_waitcnt immediate that waits until at most n (< 64) of this wave's
 // vector-memory operations are outstanding (vmcnt is split over bits 3:0 and
 // 15:14; expcnt and lgkmcnt are left at their maxima).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// Same copy from a wave-uniform base plus a 32-bit per-lane byte offset, so
-// the load can use scalar-base addressing with no per-lane 64-bit math.
-__device__ __forceinline__ void load_lds16_off(const void* base, uint32_t off_bytes, void* lds) {
-  load_lds16(static_cast<const char*>(base) + off_bytes, lds);
-}
-
-// The same copy issued through the buffer path (buffer_load_dwordx4 ... lds)
-// from a wave-uniform base.  The compiler treats the global form as an access
-// that may touch LDS through FLAT, so while one is in flight every wait for an
-// LDS operand read drains all of them (lgkmcnt(0)); with the buffer form the
-// copy counts on vmcnt alone and reads issued ahead keep exact partial waits.
+// Asynchronous 16-byte HBM -> LDS copy (buffer_load_dwordx4 ... lds) from a
+// wave-uniform base plus a 32-bit per-lane byte offset.  `lds` must be the
+// same for every lane of the wave: lane l's 16 bytes land at lds + 16*l.  The
+// buffer form, not the global one (global_load_lds_dwordx4): the compiler
+// treats the global form as a FLAT access that may touch LDS, so while one
+// is in flight every wait for an LDS operand read drains all of them
+// (lgkmcnt(0)); the buffer form counts on vmcnt alone and reads issued ahead
+// keep exact partial waits.
 // Descriptor: base, no stride, no range limit, 32-bit data format.  A base
 // the compiler cannot prove wave-uniform makes it loop over the base's
 // distinct values, so callers pass bases computed from uniform values only.

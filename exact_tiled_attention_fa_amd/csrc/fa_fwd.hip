@@ -12,10 +12,12 @@
 // wavefronts so each row's statistics stay in one wavefront's registers.
 //
 // gfx950 mapping (one workgroup = 4 wave64 = 128 query rows):
-//   * K and V tiles of BN keys stream HBM -> LDS with global_load_lds_dwordx4
-//     (no VGPR round trip), double-buffered, K one tile ahead of V: while
-//     tile t's probabilities are formed, S of tile t+1 is computed; one
-//     barrier per tile.  Rows are stored row-major
+//   * K and V tiles of BN keys stream HBM -> LDS with buffer_load_dwordx4
+//     ... lds (no VGPR round trip) through four stages (two for the split
+//     waves at D = 256), K one tile ahead of V: while tile t's probabilities
+//     are formed, S of tile t+1 is computed; one barrier per tile.  The LDS
+//     operand reads of each MFMA are issued two MFMAs ahead of it.  Rows are
+//     stored row-major
 //     with their 16-byte chunks XOR-swizzled by row so that the MFMA operand
 //     reads below hit distinct LDS banks.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: A = K rows from LDS
@@ -85,17 +87,19 @@ template <int D> constexpr int fwd_waves() { return fwd_split<D>() ? 2 * kFwdWav
 #define FA_FWD_BN_D128 32
 #endif
 #ifndef FA_FWD_STAGES
-#define FA_FWD_STAGES 2
+#define FA_FWD_STAGES 4
 #endif
 // K/V tiles in flight: tile t+NS-1 (and K one further) is requested while
 // tile t is computed, which covers the HBM/L2 latency of the copies.
-constexpr int kStages = FA_FWD_STAGES;
+// The split waves at D = 256 keep two stages: their score exchange fills
+// the rest of the LDS.
+template <int D> constexpr int fwd_stages() { return D == 256 ? 2 : FA_FWD_STAGES; }
 #ifndef FA_FWD_PF
 #define FA_FWD_PF 2
 #endif
 // LDS operand reads issued this many MFMAs ahead of their use.
 constexpr int kPF = FA_FWD_PF;
-static_assert(kStages == 2 || kStages == 4, "stage count");
+static_assert(FA_FWD_STAGES == 2 || FA_FWD_STAGES == 4, "stage count");
 
 template <int D> struct FwdTile { static constexpr int BN = FA_FWD_BN_D64; };
 template <> struct FwdTile<128> { static constexpr int BN = FA_FWD_BN_D128; };
@@ -140,6 +144,7 @@ void fwd_kernel(const FwdParams prm) {
   constexpr int DH = SPLIT ? D / 2 : D;      // head dims per wave
   constexpr int BM = kFwdBM;
   constexpr int BN = FwdTile<D>::BN;
+  constexpr int kStages = fwd_stages<D>();
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = BN * D;               // elements per K or V tile
   constexpr int NLOAD = BN * CPR / NT;       // LDS-direct loads per thread per tile (each of K, V)

@@ -56,12 +56,14 @@ void check_fwd_map(int B, int Hq, int Hkv, int nqt, int bpc) {
 }
 
 // Replay of the prefill kernel's walk for one workgroup (rows q0 ..
-// q0+BM-1 of a sequence), mirroring its pipeline step: K(t+NS) and
+// q0+BM-1 of a sequence) with kNS K/V stages (4 at D = 64 and 128, 2 for the
+// split waves at D = 256), mirroring its pipeline step: K(t+NS) and
 // V(t+NS-1) are requested at step t (clamped in the masked phases, unclamped
 // in the main phase), then S(t+1), P(t) and P(t).V(t) are formed for the
 // waves that see those tiles.
-constexpr int kBM = 128, kRows = 32, kWaves = 4, kNS = 2;
+constexpr int kBM = 128, kRows = 32, kWaves = 4;
 
+template <int kNS>
 void check_walk(int Lq, int Lk, bool causal, int wl, int wr, int BN) {
   const fa::KeyRange kr(Lq, Lk, causal, wl, wr);
   for (int q0 = 0; q0 < Lq; q0 += kBM) {
@@ -89,8 +91,8 @@ void check_walk(int Lq, int Lk, bool causal, int wl, int wr, int BN) {
       }
     }
     char tag[160];
-    std::snprintf(tag, sizeof tag, "walk Lq=%d Lk=%d causal=%d win=(%d,%d) BN=%d q0=%d", Lq, Lk,
-                  (int)causal, wl, wr, BN, q0);
+    std::snprintf(tag, sizeof tag, "walk NS=%d Lq=%d Lk=%d causal=%d win=(%d,%d) BN=%d q0=%d",
+                  kNS, Lq, Lk, (int)causal, wl, wr, BN, q0);
     const int tf = walk.t_first;
     auto visible_whole = [&](int u) {  // every row of the workgroup sees tile u whole
       const int j0 = (tf + u) * BN;
@@ -179,12 +181,19 @@ int main() {
   for (int Lq : lens)
     for (int Lk : lens)
       for (int causal = 0; causal < 2; ++causal)
-        for (const auto& w : wins) check_walk(Lq, Lk, causal != 0, w[0], w[1], 32);
+        for (const auto& w : wins) {
+          check_walk<2>(Lq, Lk, causal != 0, w[0], w[1], 32);
+          check_walk<4>(Lq, Lk, causal != 0, w[0], w[1], 32);
+        }
   for (int causal = 0; causal < 2; ++causal) {
-    check_walk(4096, 4096, causal != 0, -1, -1, 32);
-    check_walk(16384, 16384, causal != 0, 4095, 0, 32);
-    check_walk(1, 4096, causal != 0, -1, -1, 32);
-    check_walk(129, 4097, causal != 0, -1, -1, 32);
+    check_walk<2>(4096, 4096, causal != 0, -1, -1, 32);
+    check_walk<4>(4096, 4096, causal != 0, -1, -1, 32);
+    check_walk<2>(16384, 16384, causal != 0, 4095, 0, 32);
+    check_walk<4>(16384, 16384, causal != 0, 4095, 0, 32);
+    check_walk<2>(1, 4096, causal != 0, -1, -1, 32);
+    check_walk<4>(1, 4096, causal != 0, -1, -1, 32);
+    check_walk<2>(129, 4097, causal != 0, -1, -1, 32);
+    check_walk<4>(129, 4097, causal != 0, -1, -1, 32);
   }
   if (failures) {
     std::printf("%d failures\n", failures);
